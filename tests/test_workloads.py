@@ -1,0 +1,117 @@
+"""Seeded generators: determinism, shapes, ranges, and the structure each
+workload promises (distinct blocks, prefix sharing, copy pairs)."""
+
+import numpy as np
+
+import oracle
+from paged_kv_cache_91_amd import workloads as W
+
+
+def _same(a, b):
+    for f in ("q", "k_pool", "v_pool", "block_tables", "context_lens"):
+        assert np.array_equal(getattr(a, f), getattr(b, f)), f
+
+
+def test_deterministic():
+    _same(W.config1(), W.config1())
+    _same(W.config2(num_seqs=4, ctx_range=(1, 50), num_blocks=64),
+          W.config2(num_seqs=4, ctx_range=(1, 50), num_blocks=64))
+    a = W.config2(seed=9, num_seqs=4, ctx_range=(1, 50), num_blocks=64)
+    b = W.config2(seed=10, num_seqs=4, ctx_range=(1, 50), num_blocks=64)
+    assert not np.array_equal(a.q, b.q)
+
+
+def test_normal_stream_independent_of_threads(monkeypatch):
+    x = W.normal_f32(3, 1, (1 << 20) * 2 + 17)
+    monkeypatch.setattr(W.os, "sched_getaffinity", lambda pid: {0})
+    y = W.normal_f32(3, 1, (1 << 20) * 2 + 17)
+    assert np.array_equal(x, y)
+    assert abs(float(x.mean())) < 0.01 and abs(float(x.std()) - 1) < 0.01
+
+
+def test_config1_shape():
+    wl = W.config1()
+    assert wl.q.shape == (2, 1, 8) and wl.k_pool.shape == (16, 1, 4, 8)
+    assert list(wl.context_lens) == [6, 3]
+    t = wl.block_tables
+    ids = [t[0, 0], t[0, 1], t[1, 0]]
+    assert len(set(ids)) == 3 and all(0 <= i < 16 for i in ids)
+    assert wl.scale == float(np.float32(1 / np.sqrt(8)))
+
+
+def test_config2_small_structure():
+    wl = W.config2(num_seqs=8, ctx_range=(1, 300), num_blocks=256)
+    assert wl.q.dtype == np.uint16 and wl.k_pool.shape == (256, 8, 16, 128)
+    assert wl.group == 4
+    used = np.concatenate([wl.block_tables[s, :-(-int(n) // 16)]
+                           for s, n in enumerate(wl.context_lens)])
+    assert len(np.unique(used)) == len(used)
+    assert wl.kv_bytes() == int(wl.context_lens.sum()) * 2 * 8 * 128 * 2
+
+
+def test_config2_full_lengths_only():
+    rng = np.random.default_rng(2)
+    lens = rng.integers(128, 2049, size=64)
+    assert lens.min() >= 128 and lens.max() <= 2048
+
+
+def test_config3_lognormal_and_write():
+    rng = np.random.default_rng(0)
+    lens = W.lognormal_lengths(rng, 200000)
+    assert 490 <= np.median(lens) <= 535 and lens.min() >= 16 and lens.max() <= 4096
+    wl = W.config3(num_seqs=6, num_blocks=512, length_cap=200)
+    assert wl.write_k.shape == (6, 40, 128) and wl.slot_mapping.shape == (6,)
+    for s, n in enumerate(wl.context_lens):
+        slot = int(wl.slot_mapping[s])
+        assert slot // 16 == wl.block_tables[s, (n - 1) // 16] and slot % 16 == (n - 1) % 16
+
+
+def test_config4_prefix_and_copy_pairs():
+    wl = W.config4(num_blocks=2048)
+    assert wl.copy_pairs.shape == (16, 2)
+    src = set(wl.copy_pairs[:, 0])
+    assert len(src) == 1
+    p4 = int(wl.copy_pairs[0, 0])
+    before, after = wl.tables_before_copy, wl.block_tables
+    assert all(before[s, 4] == p4 for s in range(64))
+    assert all(after[s, 4] == wl.copy_pairs[s, 1] for s in range(16))
+    assert all(after[s, 4] == p4 for s in range(16, 64))
+    assert np.array_equal(before[:, :4], after[:, :4])
+    assert len(set(wl.copy_pairs[:, 1])) == 16 and not (set(wl.copy_pairs[:, 1]) & src)
+    assert wl.meta["prefix_refcount_after"] == 48
+    assert (wl.context_lens >= 81).all() and (wl.context_lens <= 380).all()
+    # the copy destinations hold nothing until the copy runs
+    assert not wl.k_pool[wl.copy_pairs[:, 1]].any()
+
+
+def test_config5_small_write_side():
+    wl = W.config5(num_seqs=3, ctx_range=(100, 700), num_blocks=128)
+    n = int(wl.context_lens.sum())
+    assert wl.write_k.shape == (n, 8, 128) and wl.slot_mapping.shape == (n,)
+    assert len(np.unique(wl.slot_mapping)) == n
+    assert wl.slot_mapping.max() < 128 * 32
+    amax = np.abs(W.bf16_bits_to_f32(wl.write_k)).max()
+    assert wl.k_scale == float(np.float32(amax) / np.float32(448))
+    rows = W.sequence_rows(wl, [1])
+    assert len(rows) == wl.context_lens[1]
+
+
+def test_relocate_keeps_logical_contents():
+    wl = W.config2(num_seqs=5, ctx_range=(1, 90), num_blocks=64)
+    other = W.relocate(wl, 5)
+    for s, n in enumerate(wl.context_lens):
+        assert np.array_equal(oracle.gather_kv(wl.k_pool, wl.block_tables[s], int(n)),
+                              oracle.gather_kv(other.k_pool, other.block_tables[s], int(n)))
+
+
+def test_poison_layout():
+    wl = W.config2(num_seqs=4, ctx_range=(1, 40), num_blocks=32, poison=True)
+    pad = wl.meta["pad_block"]
+    assert (wl.k_pool[pad] == W.NAN_BITS["bf16"]).all()
+    for s, n in enumerate(wl.context_lens):
+        nb = -(-int(n) // 16)
+        assert (wl.block_tables[s, nb:] == pad).all()
+        if n % 16:
+            assert (wl.k_pool[wl.block_tables[s, nb - 1], :, n % 16:, :] == W.NAN_BITS["bf16"]).all()
+        g = oracle.gather_kv(wl.k_pool, wl.block_tables[s], int(n))
+        assert not np.isnan(oracle.to_float64(g, "bf16")).any()
