@@ -1,0 +1,200 @@
+/*
+ * pa.h -- C ABI of libpa.so, the MI355X (gfx950) paged KV-cache hot path.
+ *
+ * Three operations:
+ *
+ *   pa_write_kv     scatter new K/V rows into the paged pool through a slot
+ *                   mapping (the cache write);
+ *   pa_decode       single-token attention for a batch of sequences, reading
+ *                   K/V through per-sequence block tables, optionally split
+ *                   over the context with a log-sum-exp merge;
+ *   pa_copy_blocks  whole-block copies, the copy-on-write step for shared
+ *                   prefix blocks.
+ *
+ * Pages that define the operations (cited by title and section):
+ *   - ultralytics.com glossary "PagedAttention", section "페이징의 작동 방식":
+ *     a pool of fixed-size blocks shared by all requests, a per-request block
+ *     table, position pos stored at [table[pos / bs], pos % bs], and the
+ *     attention kernel reading the blocks back in table order;
+ *   - vasteelab.pages.dev "PagedAttentionとは？LLMのKV Cacheをblock単位で管理する",
+ *     section "PagedAttentionはAttention kernelとmemory managerの組み合わせである":
+ *     K and V are written through physical blocks and a slot mapping, and the
+ *     model runner hands the mapping to the kernel;
+ *   - gufacode.com "PagedAttention:KV cache 的页表革命", section
+ *     "PagedAttention CUDA Kernel": per sequence, gather the blocks the table
+ *     names and compute softmax(q K^T) V;
+ *   - vasteelab.pages.dev, section "Copy-on-Writeで共通prefixを共有できる", and
+ *     ultralytics.com, section "시퀀스 간 블록 공유": a block still shared by
+ *     other sequences is copied to a fresh block before a sequence writes it.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every array pointer is DEVICE memory owned by the caller (for instance a
+ *   torch tensor's data_ptr()), row-major and contiguous.  The pa_kv_pool
+ *   descriptor itself is HOST memory and is read during the call only.
+ * - The library never allocates, frees or synchronises.  Work is enqueued on
+ *   `stream` (a hipStream_t; NULL means the default stream) and the call
+ *   returns immediately.  Faults during kernel execution surface at the
+ *   caller's next synchronisation on that stream.
+ * - Every call returns a pa_status.  Argument errors are found on the host
+ *   before anything is enqueued; nothing is enqueued when a call fails.
+ *   pa_last_error() then gives a one-line reason (per thread).
+ * - Pool layout: K and V are separate arrays, each
+ *       [num_blocks][num_kv_heads][block_size][head_dim]
+ *   so one (block, head) tile of block_size x head_dim elements is
+ *   contiguous.  block_size is a power of two in [2, 256]; head_dim is one of
+ *   8, 64, 128, 256.
+ * - Element types: PA_F32 (IEEE binary32), PA_F16 (IEEE binary16), PA_BF16
+ *   (bfloat16), PA_FP8_E4M3 (OCP 8-bit e4m3 "fn": bias 7, max 448, no
+ *   infinities).  An fp8 pool holds code * scale, with one float scale per
+ *   tensor (k_scale for K, v_scale for V).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's hipStream_t (declared here so this header does not need
+ * the HIP headers). */
+struct ihipStream_t;
+typedef struct ihipStream_t *pa_stream_t;
+
+typedef enum {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2,
+  PA_FP8_E4M3 = 3
+} pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1, /* null pointer, negative size, shape mismatch */
+  PA_ERR_UNSUPPORTED = -2, /* valid but not built: head_dim, dtype combination */
+  PA_ERR_WORKSPACE = -3,   /* split-KV workspace missing or too small */
+  PA_ERR_HIP = -4          /* the HIP runtime refused the launch */
+} pa_status;
+
+/* Describes a caller-owned K/V pool pair. */
+typedef struct {
+  void *k_pool;          /* device, [num_blocks][num_kv_heads][block_size][head_dim] */
+  void *v_pool;          /* device, same shape and dtype as k_pool */
+  int64_t num_blocks;    /* N >= 1 */
+  int32_t num_kv_heads;  /* Hkv >= 1 */
+  int32_t block_size;    /* bs: power of two in [2, 256] */
+  int32_t head_dim;      /* D: 8, 64, 128 or 256 */
+  int32_t dtype;         /* pa_dtype of the stored elements */
+  float k_scale;         /* fp8 pools: K = code * k_scale (> 0, finite); else must be 1 */
+  float v_scale;         /* fp8 pools: V = code * v_scale (> 0, finite); else must be 1 */
+} pa_kv_pool;
+
+/*
+ * pa_write_kv -- the cache write (reshape_and_cache).
+ *
+ * For every token t < num_tokens with s = slot_mapping[t], and every KV head h:
+ *     pool[s / bs][h][s % bs][:] = row[t][h][:]
+ * for K (from k) and V (from v).
+ *
+ *   k, v          device, [num_tokens][num_kv_heads][head_dim] of src_dtype.
+ *   src_dtype     equal to pool->dtype (the bits are copied), or PA_F32 /
+ *                 PA_F16 / PA_BF16 when pool->dtype is PA_FP8_E4M3: then each
+ *                 element is widened to float, multiplied in float by
+ *                 (1.0f / scale) and encoded to e4m3 with round-to-nearest-even,
+ *                 saturating to +-448 (NaN stays NaN).
+ *   slot_mapping  device, int64 [num_tokens]; slots must be distinct and lie
+ *                 in [0, num_blocks * bs).  A slot outside that range is
+ *                 skipped (its token is not written) rather than faulting.
+ *   num_tokens    >= 0; 0 enqueues nothing.
+ * Tokens are independent: the call has no ordering between them.
+ */
+int pa_write_kv(const void *k, const void *v, int32_t src_dtype, int32_t num_tokens,
+                const int64_t *slot_mapping, const pa_kv_pool *pool, pa_stream_t stream);
+
+/*
+ * pa_decode_workspace_bytes -- device scratch pa_decode needs in split mode:
+ * float32 partial maxima, sums and outputs for every (sequence, query head,
+ * partition), with ceil(max_blocks_per_seq * block_size / partition_size)
+ * partitions per sequence.  Returns 0 for partition_size == 0 (single pass)
+ * and for invalid arguments.
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_blocks_per_seq, int32_t block_size,
+                                 int32_t partition_size);
+
+/*
+ * pa_decode -- paged single-token attention.
+ *
+ * For every sequence s < num_seqs with n = context_lens[s], and every query
+ * head h < num_q_heads, with kv = h / (num_q_heads / num_kv_heads)
+ * (contiguous grouping of query heads onto shared KV heads):
+ *     K_i = k_pool[block_tables[s][i / bs]][kv][i % bs][:]   for i < n
+ *     z_i = scale * <q[s][h], K_i>
+ *     out[s][h][:] = sum_i softmax(z)_i * V_i
+ * computed with float32 accumulation.  Positions i >= n in the last block
+ * never contribute; n == 0 gives a zero row.  The result does not depend on
+ * where the blocks physically lie: the accumulation order is a function of
+ * the logical positions only, so relabelling the physical blocks gives
+ * bit-identical output.
+ *
+ *   q             device, [num_seqs][num_q_heads][head_dim] of q_dtype.
+ *   q_dtype       PA_F32, PA_F16 or PA_BF16.  Built combinations of
+ *                 (q_dtype, pool->dtype): (F32,F32), (F16,F16), (BF16,BF16),
+ *                 (BF16,FP8_E4M3), (F16,FP8_E4M3).
+ *   num_q_heads   a multiple of pool->num_kv_heads.
+ *   block_tables  device, int32 [num_seqs][max_blocks_per_seq]; entries
+ *                 j < ceil(n / bs) must lie in [0, num_blocks); later entries
+ *                 are never read.  A sequence whose table names a block
+ *                 outside the pool gets a NaN output row instead of a fault.
+ *   context_lens  device, int32 [num_seqs]; 0 <= n <= max_blocks_per_seq * bs
+ *                 (a sequence outside that range gets a NaN row).
+ *   scale         softmax scale (typically 1/sqrt(head_dim)); finite.
+ *   out           device, [num_seqs][num_q_heads][head_dim] of q_dtype,
+ *                 rounded to nearest even from float32.  Must not overlap q.
+ *   partition_size  0: single pass, one workgroup walks a whole context.
+ *                 > 0: split-KV; a multiple of bs; partition p covers
+ *                 positions [p*P, min((p+1)*P, n)); the partial results are
+ *                 merged in increasing p by a second kernel on the same
+ *                 stream.
+ *   workspace     device scratch of at least pa_decode_workspace_bytes(...)
+ *                 bytes when partition_size > 0 (else may be NULL).  Its
+ *                 contents on entry do not matter.  Concurrent calls must not
+ *                 share one workspace.
+ */
+int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+              const pa_kv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+              const int32_t *context_lens, float scale, void *out, int32_t partition_size,
+              void *workspace, size_t workspace_bytes, pa_stream_t stream);
+
+/*
+ * pa_copy_blocks -- copy-on-write block copy.
+ *
+ * For each pair i < num_pairs, (src, dst) = (src_dst_pairs[2i], src_dst_pairs[2i+1]):
+ *     k_pool[dst] = k_pool[src];  v_pool[dst] = v_pool[src]
+ * over every head and slot of the block.  Destinations must be distinct and
+ * must not also appear as sources (then the pairs commute).  A pair naming a
+ * block outside [0, num_blocks), or with src == dst, is skipped.
+ *
+ *   src_dst_pairs  device, int64 [num_pairs][2].
+ *   num_pairs      >= 0; 0 enqueues nothing.
+ */
+int pa_copy_blocks(const pa_kv_pool *pool, const int64_t *src_dst_pairs, int32_t num_pairs,
+                   pa_stream_t stream);
+
+/* Static text for a pa_status value. */
+const char *pa_status_string(int status);
+
+/* One-line reason for the calling thread's last failed call ("" if none). */
+const char *pa_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,250 @@
+// C ABI of libpa.so: argument validation, kernel selection and launch.
+// Declarations, layouts and the error contract are in include/pa.h.
+//
+// Every check runs on the host before anything is enqueued; a failing call
+// enqueues nothing and records a one-line reason for pa_last_error().
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return PA_OK;
+}
+
+int element_size(int dtype) {
+  switch (dtype) {
+    case PA_F32: return 4;
+    case PA_F16: return 2;
+    case PA_BF16: return 2;
+    case PA_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+int log2_exact(int v) {
+  if (v <= 0 || (v & (v - 1))) return -1;
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+
+bool supported_head_dim(int d) { return d == 8 || d == 64 || d == 128 || d == 256; }
+
+int check_pool(const pa_kv_pool *p) {
+  if (!p) return fail(PA_ERR_INVALID_ARG, "pool descriptor is NULL");
+  if (!p->k_pool || !p->v_pool) return fail(PA_ERR_INVALID_ARG, "pool K or V pointer is NULL");
+  if (p->k_pool == p->v_pool) return fail(PA_ERR_INVALID_ARG, "K and V pools alias");
+  if (p->num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks must be positive");
+  if (p->num_kv_heads <= 0) return fail(PA_ERR_INVALID_ARG, "num_kv_heads must be positive");
+  if (p->block_size < 2 || p->block_size > 256 || log2_exact(p->block_size) < 0)
+    return fail(PA_ERR_INVALID_ARG, "block_size %d is not a power of two in [2, 256]", p->block_size);
+  if (element_size(p->dtype) == 0) return fail(PA_ERR_INVALID_ARG, "unknown pool dtype %d", p->dtype);
+  if (!supported_head_dim(p->head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not built (8, 64, 128, 256)", p->head_dim);
+  if (p->dtype == PA_FP8_E4M3) {
+    if (!(p->k_scale > 0.0f) || !std::isfinite(p->k_scale) || !(p->v_scale > 0.0f) ||
+        !std::isfinite(p->v_scale))
+      return fail(PA_ERR_INVALID_ARG, "fp8 pool scales must be finite and positive");
+  } else if (p->k_scale != 1.0f || p->v_scale != 1.0f) {
+    return fail(PA_ERR_INVALID_ARG, "scales must be 1 for a non-fp8 pool");
+  }
+  // block bytes and slot counts must fit the kernels' 64-bit offsets
+  const double bytes = static_cast<double>(p->num_blocks) * p->num_kv_heads * p->block_size *
+                       p->head_dim * element_size(p->dtype);
+  if (bytes > 9.0e18) return fail(PA_ERR_INVALID_ARG, "pool too large");
+  return PA_OK;
+}
+
+int hip_fail(hipError_t e) {
+  return fail(PA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" {
+
+const char *pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+    default: return "PA_ERR_UNKNOWN";
+  }
+}
+
+const char *pa_last_error(void) { return g_last_error; }
+
+int pa_version(void) { return 100; }
+
+int pa_write_kv(const void *k, const void *v, int32_t src_dtype, int32_t num_tokens,
+                const int64_t *slot_mapping, const pa_kv_pool *pool, pa_stream_t stream) {
+  if (int st = check_pool(pool)) return st;
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens must be >= 0");
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "k, v or slot_mapping is NULL");
+  if (element_size(src_dtype) == 0) return fail(PA_ERR_INVALID_ARG, "unknown source dtype %d", src_dtype);
+  if (src_dtype != pool->dtype &&
+      !(pool->dtype == PA_FP8_E4M3 && src_dtype != PA_FP8_E4M3))
+    return fail(PA_ERR_UNSUPPORTED, "write from dtype %d into pool dtype %d not built", src_dtype,
+                pool->dtype);
+  pa_impl::WriteArgs a{};
+  a.k = k;
+  a.v = v;
+  a.slots = slot_mapping;
+  a.k_pool = pool->k_pool;
+  a.v_pool = pool->v_pool;
+  a.num_slots = pool->num_blocks * pool->block_size;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim;
+  a.bs_log2 = log2_exact(pool->block_size);
+  a.k_inv = 1.0f / pool->k_scale;
+  a.v_inv = 1.0f / pool->v_scale;
+  const int64_t total_units = static_cast<int64_t>(num_tokens) * pool->num_kv_heads * pool->head_dim;
+  if (total_units / 4 / 256 > 0x7fffffffLL) return fail(PA_ERR_INVALID_ARG, "too many tokens");
+  bool supported = true;
+  hipError_t e = pa_impl::launch_write(src_dtype, pool->dtype, a,
+                                       reinterpret_cast<hipStream_t>(stream), &supported);
+  if (!supported) return fail(PA_ERR_UNSUPPORTED, "write combination not built");
+  if (e != hipSuccess) return hip_fail(e);
+  return ok();
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_blocks_per_seq, int32_t block_size,
+                                 int32_t partition_size) {
+  if (partition_size <= 0 || num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 ||
+      max_blocks_per_seq <= 0 || block_size <= 0)
+    return 0;
+  const int64_t parts = ceil_div(static_cast<int64_t>(max_blocks_per_seq) * block_size, partition_size);
+  const int64_t rows = static_cast<int64_t>(num_seqs) * num_q_heads * parts;
+  return static_cast<size_t>(rows) * (static_cast<size_t>(head_dim) + 2) * sizeof(float);
+}
+
+int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+              const pa_kv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+              const int32_t *context_lens, float scale, void *out, int32_t partition_size,
+              void *workspace, size_t workspace_bytes, pa_stream_t stream) {
+  if (int st = check_pool(pool)) return st;
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 0");
+  if (num_seqs == 0) return ok();
+  if (num_seqs > 65535) return fail(PA_ERR_INVALID_ARG, "num_seqs %d above 65535", num_seqs);
+  if (!q || !out || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "q, out, block_tables or context_lens is NULL");
+  if (q == out) return fail(PA_ERR_INVALID_ARG, "out must not alias q");
+  if (num_q_heads <= 0 || num_q_heads % pool->num_kv_heads)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                num_q_heads, pool->num_kv_heads);
+  if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
+  if (static_cast<int64_t>(max_blocks_per_seq) * pool->block_size > 0x7fffffffLL)
+    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq * block_size overflows int32");
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+  if (q_dtype != PA_F32 && q_dtype != PA_F16 && q_dtype != PA_BF16)
+    return fail(PA_ERR_INVALID_ARG, "q dtype must be F32, F16 or BF16");
+  const bool combo = (q_dtype == pool->dtype) ||
+                     (pool->dtype == PA_FP8_E4M3 && (q_dtype == PA_BF16 || q_dtype == PA_F16));
+  if (!combo) return fail(PA_ERR_UNSUPPORTED, "q dtype %d with pool dtype %d not built", q_dtype, pool->dtype);
+  if (partition_size < 0) return fail(PA_ERR_INVALID_ARG, "partition_size must be >= 0");
+  if (partition_size > 0 && partition_size % pool->block_size)
+    return fail(PA_ERR_INVALID_ARG, "partition_size %d is not a multiple of block_size %d",
+                partition_size, pool->block_size);
+
+  const int group = num_q_heads / pool->num_kv_heads;
+  int hpw = 1;
+  while (hpw < group && hpw < 8) hpw <<= 1;
+  const int head_groups = static_cast<int>(ceil_div(group, hpw));
+  if (static_cast<int64_t>(pool->num_kv_heads) * head_groups > 65535)
+    return fail(PA_ERR_INVALID_ARG, "too many heads");
+
+  pa_impl::DecodeArgs a{};
+  a.q = q;
+  a.k_pool = pool->k_pool;
+  a.v_pool = pool->v_pool;
+  a.tables = block_tables;
+  a.ctx = context_lens;
+  a.out = out;
+  a.num_blocks = pool->num_blocks;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.group = group;
+  a.heads_per_wg = hpw;
+  a.head_groups = head_groups;
+  a.head_dim = pool->head_dim;
+  a.block_size = pool->block_size;
+  a.bs_log2 = log2_exact(pool->block_size);
+  a.max_blocks = max_blocks_per_seq;
+  a.partition_size = partition_size;
+  a.max_parts = 1;
+  const double log2e = 1.4426950408889634;
+  const double ks = pool->dtype == PA_FP8_E4M3 ? static_cast<double>(pool->k_scale) : 1.0;
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * ks * log2e);
+  a.v_scale = pool->dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
+
+  if (partition_size > 0) {
+    const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, pool->head_dim,
+                                                  max_blocks_per_seq, pool->block_size, partition_size);
+    if (!workspace || workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "split-KV workspace needs %zu bytes, got %zu", need,
+                  workspace ? workspace_bytes : static_cast<size_t>(0));
+    const int64_t parts = ceil_div(static_cast<int64_t>(max_blocks_per_seq) * pool->block_size, partition_size);
+    a.max_parts = static_cast<int32_t>(parts);
+    const int64_t rows = static_cast<int64_t>(num_seqs) * num_q_heads * parts;
+    float *ws = static_cast<float *>(workspace);
+    a.part_m = ws;
+    a.part_l = ws + rows;
+    a.part_o = ws + 2 * rows;
+  }
+  bool supported = true;
+  hipError_t e = pa_impl::launch_decode(q_dtype, pool->dtype, a, reinterpret_cast<hipStream_t>(stream),
+                                        &supported);
+  if (!supported) return fail(PA_ERR_UNSUPPORTED, "decode specialisation not built");
+  if (e != hipSuccess) return hip_fail(e);
+  return ok();
+}
+
+int pa_copy_blocks(const pa_kv_pool *pool, const int64_t *src_dst_pairs, int32_t num_pairs,
+                   pa_stream_t stream) {
+  if (int st = check_pool(pool)) return st;
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "num_pairs must be >= 0");
+  if (num_pairs == 0) return ok();
+  if (!src_dst_pairs) return fail(PA_ERR_INVALID_ARG, "src_dst_pairs is NULL");
+  pa_impl::CopyArgs a{};
+  a.k_pool = pool->k_pool;
+  a.v_pool = pool->v_pool;
+  a.pairs = src_dst_pairs;
+  a.num_blocks = pool->num_blocks;
+  a.block_bytes = static_cast<int64_t>(pool->num_kv_heads) * pool->block_size * pool->head_dim *
+                  element_size(pool->dtype);
+  a.num_pairs = num_pairs;
+  if (ceil_div(a.block_bytes, 4096) > 65535) return fail(PA_ERR_INVALID_ARG, "block too large");
+  hipError_t e = pa_impl::launch_copy(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Internal interface between the C ABI layer (pa_api.cpp) and the HIP
+// kernels (pa_kernels.hip).  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace pa_impl {
+
+// Element storage codes; equal to the public pa_dtype values.
+enum Dt : int { kF32 = 0, kF16 = 1, kBF16 = 2, kFP8 = 3 };
+
+struct DecodeArgs {
+  const void *q;
+  const void *k_pool;
+  const void *v_pool;
+  const int32_t *tables;   // [S][max_blocks]
+  const int32_t *ctx;      // [S]
+  void *out;               // [S][Hq][D]
+  float *part_m;           // split mode: [S][Hq][max_parts]
+  float *part_l;           // split mode: [S][Hq][max_parts]
+  float *part_o;           // split mode: [S][Hq][max_parts][D]
+  int64_t num_blocks;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;           // Hq / Hkv
+  int32_t heads_per_wg;    // power of two <= 8
+  int32_t head_groups;     // ceil(group / heads_per_wg)
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t bs_log2;
+  int32_t max_blocks;
+  int32_t partition_size;  // 0 = single pass
+  int32_t max_parts;       // partitions per sequence in the workspace (1 if single pass)
+  float scale_log2;        // scale * k_scale * log2(e)
+  float v_scale;           // 1 unless fp8
+};
+
+struct WriteArgs {
+  const void *k;
+  const void *v;
+  const int64_t *slots;
+  void *k_pool;
+  void *v_pool;
+  int64_t num_slots;       // num_blocks * block_size
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t bs_log2;
+  float k_inv;             // 1 / k_scale (fp8 destination)
+  float v_inv;
+};
+
+struct CopyArgs {
+  void *k_pool;
+  void *v_pool;
+  const int64_t *pairs;
+  int64_t num_blocks;
+  int64_t block_bytes;     // Hkv * bs * D * element size
+  int32_t num_pairs;
+};
+
+// Each returns hipSuccess or the launch error; `supported` (when given) is
+// set false for combinations no kernel was built for.
+hipError_t launch_decode(int q_dtype, int kv_dtype, const DecodeArgs &a, hipStream_t s,
+                         bool *supported);
+hipError_t launch_write(int src_dtype, int dst_dtype, const WriteArgs &a, hipStream_t s,
+                        bool *supported);
+hipError_t launch_copy(const CopyArgs &a, hipStream_t s);
+
+}  // namespace pa_impl

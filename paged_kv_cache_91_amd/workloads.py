@@ -358,48 +358,67 @@ def config4(seed: int = 4, num_seqs: int = 64, prefix_tokens: int = 80,
               "prefix_refcount_after": alloc.refcount(int(pairs[0, 0])) if len(pairs) else None})
 
 
-def config5(seed: int = 5, num_seqs: int = 32, ctx_range=(8192, 32768),
-            num_blocks: int = 32768, partition_size: int = 512,
-            poison: bool = False) -> Workload:
-    """Long-context split-KV decode over an fp8 e4m3 cache with per-tensor
-    scales and bf16 q: 64 q heads on 8 KV heads, head_dim 128, block 32.
-
-    The pools start empty (or NaN when poisoned) and are filled by the cache
-    write of every position's bf16 K/V row (``write_*`` / ``slot_mapping``);
-    each side (GPU and oracle) performs that write itself.  The scales are
-    max|row value| / 448 over all rows, as float32.
-    """
-    rng = np.random.default_rng(seed)
-    lens = rng.integers(ctx_range[0], ctx_range[1] + 1, size=num_seqs).astype(np.int32)
+def build_write_filled(seed: int, *, name: str, q_dtype: str, src_dtype: str, kv_dtype: str,
+                       num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+                       num_blocks: int, context_lens: Sequence[int], partition_size: int = 0,
+                       rng: Optional[np.random.Generator] = None,
+                       poison: bool = False) -> Workload:
+    """Workload whose pools start empty (or NaN when poisoned) and are filled
+    by the cache write of every position's K/V row (``write_*`` /
+    ``slot_mapping``, rows in sequence order); each side (GPU and oracle)
+    performs that write itself.  For an fp8 pool the per-tensor scales are
+    max|row value| / 448 over all rows, as float32."""
+    if rng is None:
+        rng = np.random.default_rng(seed)
+    lens = np.asarray(context_lens, dtype=np.int32)
     perm = rng.permutation(num_blocks)
-    bs, hkv, hq, d = 32, 8, 64, 128
-    alloc = BlockAllocator(num_blocks, bs, free_order=perm)
+    alloc = BlockAllocator(num_blocks, block_size, free_order=perm)
     slots = []
     for s, n in enumerate(lens):
         alloc.add_sequence(s, int(n))
         slots.append(alloc.slots(s, 0, int(n)))
-    maxb = max(len(alloc.block_table(s)) for s in range(num_seqs))
+    maxb = max(max(len(alloc.block_table(s)) for s in range(len(lens))), 1)
     pad = alloc.free_block_ids()[0] if poison else 0
-    tables = alloc.tables_array(range(num_seqs), maxb, pad=pad)
+    tables = alloc.tables_array(range(len(lens)), maxb, pad=pad)
     slot_mapping = np.concatenate(slots).astype(np.int64)
     t = len(slot_mapping)
-    k_rows = cast_f32(normal_f32(seed, _S_K, t * hkv * d), "bf16").reshape(t, hkv, d)
-    v_rows = cast_f32(normal_f32(seed, _S_V, t * hkv * d), "bf16").reshape(t, hkv, d)
-    k_scale = float(np.float32(np.abs(bf16_bits_to_f32(k_rows)).max()) / np.float32(448.0))
-    v_scale = float(np.float32(np.abs(bf16_bits_to_f32(v_rows)).max()) / np.float32(448.0))
-    shape = (num_blocks, hkv, bs, d)
-    fill = NAN_BITS["fp8_e4m3"] if poison else np.uint8(0)
-    k_pool = np.full(shape, fill, dtype=np.uint8)
-    v_pool = np.full(shape, fill, dtype=np.uint8)
-    q = cast_f32(normal_f32(seed, _S_Q, num_seqs * hq * d), "bf16").reshape(num_seqs, hq, d)
+    hkv, d = num_kv_heads, head_dim
+    k_rows = cast_f32(normal_f32(seed, _S_K, t * hkv * d), src_dtype).reshape(t, hkv, d)
+    v_rows = cast_f32(normal_f32(seed, _S_V, t * hkv * d), src_dtype).reshape(t, hkv, d)
+    k_scale = v_scale = 1.0
+    if kv_dtype == "fp8_e4m3":
+        widen = bf16_bits_to_f32 if src_dtype == "bf16" else (lambda a: np.asarray(a, np.float32))
+        k_scale = float(np.float32(np.abs(widen(k_rows)).max()) / np.float32(448.0))
+        v_scale = float(np.float32(np.abs(widen(v_rows)).max()) / np.float32(448.0))
+    shape = (num_blocks, hkv, block_size, d)
+    fill = NAN_BITS[kv_dtype] if poison else STORAGE[kv_dtype](0)
+    k_pool = np.full(shape, fill, dtype=STORAGE[kv_dtype])
+    v_pool = np.full(shape, fill, dtype=STORAGE[kv_dtype])
+    q = cast_f32(normal_f32(seed, _S_Q, len(lens) * num_q_heads * d), q_dtype).reshape(
+        len(lens), num_q_heads, d)
     return Workload(
-        name="long-ctx-fp8-split", q_dtype="bf16", kv_dtype="fp8_e4m3", num_q_heads=hq,
-        num_kv_heads=hkv, head_dim=d, block_size=bs, num_blocks=num_blocks, q=q,
+        name=name, q_dtype=q_dtype, kv_dtype=kv_dtype, num_q_heads=num_q_heads,
+        num_kv_heads=hkv, head_dim=d, block_size=block_size, num_blocks=num_blocks, q=q,
         k_pool=k_pool, v_pool=v_pool, block_tables=tables, context_lens=lens,
         scale=float(np.float32(1.0 / math.sqrt(d))), k_scale=k_scale, v_scale=v_scale,
-        partition_size=partition_size, write_src_dtype="bf16", write_k=k_rows,
+        partition_size=partition_size, write_src_dtype=src_dtype, write_k=k_rows,
         write_v=v_rows, slot_mapping=slot_mapping,
         meta={"seed": seed, "alloc": alloc.stats(), "poison": poison, "pad_block": pad})
+
+
+def config5(seed: int = 5, num_seqs: int = 32, ctx_range=(8192, 32768),
+            num_blocks: int = 32768, partition_size: int = 512,
+            poison: bool = False) -> Workload:
+    """Long-context split-KV decode over an fp8 e4m3 cache with per-tensor
+    scales and bf16 q: 64 q heads on 8 KV heads, head_dim 128, block 32,
+    lengths uniform in ``ctx_range``; the pools are filled by the cache write
+    of every position's bf16 row (see :func:`build_write_filled`)."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(ctx_range[0], ctx_range[1] + 1, size=num_seqs).astype(np.int32)
+    return build_write_filled(seed, name="long-ctx-fp8-split", q_dtype="bf16", src_dtype="bf16",
+                              kv_dtype="fp8_e4m3", num_q_heads=64, num_kv_heads=8, head_dim=128,
+                              block_size=32, num_blocks=num_blocks, context_lens=lens,
+                              partition_size=partition_size, rng=rng, poison=poison)
 
 
 def sequence_rows(wl: Workload, seqs: Sequence[int]) -> np.ndarray:

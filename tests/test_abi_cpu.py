@@ -1,0 +1,123 @@
+"""The C ABI without a GPU: libpa.so loads, exports every function
+include/pa.h declares, and rejects bad arguments on the host before any
+launch.  Only calls that fail validation (or enqueue nothing) are made."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_91_amd import pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+FAKE = 0x10000   # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = pa.lib()
+    names = declared_functions()
+    assert set(names) == set(pa.EXPORTED)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    lib = pa.lib()
+    assert [lib.pa_status_string(s).decode() for s in (0, -1, -2, -3, -4, 7)] == [
+        "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_WORKSPACE", "PA_ERR_HIP",
+        "PA_ERR_UNKNOWN"]
+    assert lib.pa_version() >= 100
+
+
+def test_workspace_bytes():
+    # rows = S * Hq * ceil(maxb * bs / P); each row holds m, l and D outputs
+    assert pa.pa_decode_workspace_bytes(32, 64, 128, 1024, 32, 512) == 32 * 64 * 64 * 130 * 4
+    assert pa.pa_decode_workspace_bytes(3, 2, 8, 5, 4, 8) == 3 * 2 * 3 * 10 * 4
+    assert pa.pa_decode_workspace_bytes(3, 2, 8, 5, 4, 0) == 0
+    assert pa.pa_decode_workspace_bytes(0, 2, 8, 5, 4, 8) == 0
+
+
+def _pool(**kw):
+    base = dict(k_pool=FAKE, v_pool=FAKE * 2, num_blocks=16, num_kv_heads=2, block_size=16,
+                head_dim=128, dtype=pa.PA_BF16, k_scale=1.0, v_scale=1.0)
+    base.update(kw)
+    return pa.KvPool(**base)
+
+
+def _decode(pool, **kw):
+    args = dict(q=FAKE * 3, q_dtype=pa.PA_BF16, num_seqs=2, num_q_heads=8, tables=FAKE * 4,
+                maxb=4, ctx=FAKE * 5, scale=0.1, out=FAKE * 6, part=0, ws=None, ws_bytes=0)
+    args.update(kw)
+    return pa.lib().pa_decode(args["q"], args["q_dtype"], args["num_seqs"], args["num_q_heads"],
+                              ctypes.byref(pool) if pool is not None else None, args["tables"],
+                              args["maxb"], args["ctx"], args["scale"], args["out"], args["part"],
+                              args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("pool_kw,expect", [
+    (dict(block_size=3), -1),
+    (dict(block_size=1), -1),
+    (dict(block_size=512), -1),
+    (dict(head_dim=96), -2),
+    (dict(num_blocks=0), -1),
+    (dict(num_kv_heads=0), -1),
+    (dict(dtype=9), -1),
+    (dict(k_pool=0), -1),
+    (dict(v_pool=FAKE), -1),                       # aliases k_pool
+    (dict(dtype=pa.PA_FP8_E4M3, k_scale=0.0), -1),
+    (dict(dtype=pa.PA_FP8_E4M3, v_scale=float("inf")), -1),
+    (dict(k_scale=2.0), -1),                       # scale on a bf16 pool
+])
+def test_decode_rejects_bad_pool(pool_kw, expect):
+    assert _decode(_pool(**pool_kw)) == expect
+    assert pa.lib().pa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(num_q_heads=7), -1),                     # not a multiple of Hkv
+    (dict(num_q_heads=0), -1),
+    (dict(num_seqs=-1), -1),
+    (dict(num_seqs=70000), -1),
+    (dict(q=0), -1),
+    (dict(out=FAKE * 3), -1),                      # aliases q
+    (dict(maxb=0), -1),
+    (dict(scale=float("nan")), -1),
+    (dict(q_dtype=pa.PA_FP8_E4M3), -1),
+    (dict(q_dtype=pa.PA_F16), -2),                 # f16 q with a bf16 pool
+    (dict(part=24), -1),                           # not a multiple of block_size
+    (dict(part=-16), -1),
+    (dict(part=32), -3),                           # no workspace
+    (dict(part=32, ws=FAKE * 7, ws_bytes=16), -3), # too small
+])
+def test_decode_rejects_bad_args(kw, expect):
+    assert _decode(_pool(), **kw) == expect
+
+
+def test_decode_null_pool_and_empty_batch():
+    assert _decode(None) == -1
+    assert _decode(_pool(), num_seqs=0) == 0       # nothing to do: no launch
+
+
+def test_write_and_copy_validation():
+    lib = pa.lib()
+    p = _pool()
+    assert lib.pa_write_kv(FAKE, FAKE, pa.PA_BF16, -1, FAKE, ctypes.byref(p), None) == -1
+    assert lib.pa_write_kv(FAKE, FAKE, pa.PA_BF16, 0, FAKE, ctypes.byref(p), None) == 0
+    assert lib.pa_write_kv(0, FAKE, pa.PA_BF16, 4, FAKE, ctypes.byref(p), None) == -1
+    assert lib.pa_write_kv(FAKE, FAKE, pa.PA_F16, 4, FAKE, ctypes.byref(p), None) == -2
+    assert lib.pa_write_kv(FAKE, FAKE, 11, 4, FAKE, ctypes.byref(p), None) == -1
+    fp8 = _pool(dtype=pa.PA_FP8_E4M3, k_scale=0.5, v_scale=0.25)
+    assert lib.pa_write_kv(FAKE, FAKE, pa.PA_FP8_E4M3 + 5, 4, FAKE, ctypes.byref(fp8), None) == -1
+    assert lib.pa_copy_blocks(ctypes.byref(p), FAKE, -1, None) == -1
+    assert lib.pa_copy_blocks(ctypes.byref(p), FAKE, 0, None) == 0
+    assert lib.pa_copy_blocks(ctypes.byref(p), None, 3, None) == -1
+    assert lib.pa_copy_blocks(None, FAKE, 3, None) == -1
