@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged decode hot path on one MI355X.
+
+Workload: a Llama-3-8B-shaped decode layer in bf16 -- 32 query heads on 8 KV
+heads (group 4), head_dim 128, block size 16, 64 sequences with context
+lengths uniform in [128, 2048], blocks scattered by a seeded permutation of a
+16384-block pool (synthetic N(0,1) data).
+
+One step = the whole hot path for one layer of one decode iteration:
+  1. pa_write_kv  -- the newest token's K/V row of every sequence is written
+                     through the slot mapping (position n-1);
+  2. pa_decode    -- paged attention of every sequence over its n positions
+                     (split-KV with the log-sum-exp merge when --partition > 0).
+Steps rotate over --layers independent pools (distinct device memory, each
+its own block permutation), as consecutive layers of a model would, so the
+K/V reads come from HBM rather than from the 256 MB last-level cache.
+
+Reported (one JSON line):
+  value        KV-read GB/s of the whole step: algorithmic K/V bytes (exactly
+               context_len positions x 8 heads x 128 x 2 bytes x K and V) over
+               the synchronised wall time of the timed steps;
+  roofline     the decode call alone, timed with HIP events on its stream:
+               algorithmic bytes per launch / mean event duration, against
+               MI355X's 8 TB/s HBM peak;
+  cpu_baseline the float64 oracle (write + decode) on the same batch, on this
+               host's cores (skipped with --no-cpu-baseline).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s (10^9 bytes)
+METRIC = "paged decode KV-read GB/s and % of MI355X HBM peak; decode tokens/s/layer"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=8, help="independent layer pools to rotate over")
+    ap.add_argument("--partition", type=int, default=256,
+                    help="split-KV partition size in tokens (0 = single pass)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=64,
+                    help="sequences of the batch the oracle baseline processes")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run pa_copy_blocks over MIB MiB of blocks (counter calibration) and exit")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_91_amd import pa
+    from paged_kv_cache_91_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pa.lib()
+
+    if args.calibrate_copy:
+        return calibrate_copy(args.calibrate_copy, pa, torch, dev)
+
+    t0 = time.time()
+    wl = W.config2()
+    S, hkv, d, bs = wl.num_seqs, wl.num_kv_heads, wl.head_dim, wl.block_size
+    new_k = W.cast_f32(W.normal_f32(2, 4, S * hkv * d), "bf16").reshape(S, hkv, d)
+    new_v = W.cast_f32(W.normal_f32(2, 5, S * hkv * d), "bf16").reshape(S, hkv, d)
+    log(f"[bench] workload generated in {time.time() - t0:.1f}s: S={S} kv_bytes={wl.kv_bytes()/1e6:.1f} MB")
+
+    def bf16_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # layer 0 from the host arrays; the others are relabelled copies made on the device
+    k0, v0 = bf16_dev(wl.k_pool), bf16_dev(wl.v_pool)
+    q = bf16_dev(wl.q)
+    kn, vn = bf16_dev(new_k), bf16_dev(new_v)
+    ctx = torch.from_numpy(wl.context_lens.astype(np.int32)).to(dev)
+    pos = wl.context_lens.astype(np.int64) - 1
+    layers = []
+    for layer in range(args.layers):
+        if layer == 0:
+            perm = np.arange(wl.num_blocks)
+            kp, vp = k0, v0
+        else:
+            perm = np.random.default_rng(1000 + layer).permutation(wl.num_blocks)
+            pt = torch.from_numpy(perm).to(dev)
+            kp, vp = torch.empty_like(k0), torch.empty_like(v0)
+            kp[pt] = k0
+            vp[pt] = v0
+        tables = perm[wl.block_tables].astype(np.int32)
+        slots = tables[np.arange(S), pos // bs].astype(np.int64) * bs + pos % bs
+        layers.append(dict(
+            k=kp, v=vp, pool=pa.make_pool(kp, vp),
+            tables=torch.from_numpy(tables).to(dev), slots=torch.from_numpy(slots).to(dev)))
+    maxb = wl.max_blocks_per_seq
+    ws = None
+    if args.partition > 0:
+        ws = pa.new_workspace(S, wl.num_q_heads, hkv, d, maxb, bs, args.partition, device=dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    log(f"[bench] {args.layers} layers resident ({2 * k0.numel() * 2 * args.layers / 2**30:.1f} GiB of pools)")
+
+    def step(k, ev=None):
+        L = layers[k % len(layers)]
+        pa.pa_write_kv(kn, vn, L["slots"], L["pool"], stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        pa.pa_decode(q, L["pool"], L["tables"], ctx, wl.scale, out=out, partition_size=args.partition,
+                     workspace=ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(k, events[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    decode_ms = [a.elapsed_time(b) for a, b in events]
+    log(f"[bench] timed {args.steps} steps in {elapsed:.4f}s")
+
+    kv_bytes = wl.kv_bytes()
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = kv_bytes * args.steps / elapsed / 1e9
+    dec_mean = statistics.fmean(decode_ms)
+    dec_med = statistics.median(decode_ms)
+    achieved = kv_bytes / (dec_mean * 1e-3) / 1e9
+
+    # parity spot check of the last timed output against the first layer's oracle
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama3-8b-layer-gqa4-bf16 (Hq=32, Hkv=8, D=128, block 16, "
+                        "64 seqs, ctx U[128,2048], 16384-block pool)",
+            "num_seqs": S, "num_q_heads": wl.num_q_heads, "num_kv_heads": hkv, "head_dim": d,
+            "block_size": bs, "pool_blocks": wl.num_blocks, "context_tokens": int(wl.context_lens.sum()),
+            "partition_size": args.partition, "layers_rotated": args.layers,
+            "step": "pa_write_kv (1 token/seq) + pa_decode",
+        },
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s_per_layer": round(S / (ms_per_step * 1e-3), 1),
+        "kv_bytes_per_step": kv_bytes,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "pa_decode (decode kernel + split-KV merge)" if args.partition else "pa_decode",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "mean_us": round(dec_mean * 1e3, 2),
+            "median_us": round(dec_med * 1e3, 2),
+            "p10_us": round(sorted(decode_ms)[len(decode_ms) // 10] * 1e3, 2),
+            "p90_us": round(sorted(decode_ms)[(9 * len(decode_ms)) // 10] * 1e3, 2),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, new_k, new_v, args.cpu_seqs)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, new_k, new_v, nseq):
+    """The float64 oracle on the first ``nseq`` sequences of the same batch:
+    the same cache write (one token per sequence) and decode."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    idx = np.arange(min(nseq, wl.num_seqs))
+    bs = wl.block_size
+    pos = wl.context_lens[idx].astype(np.int64) - 1
+    slots = wl.block_tables[idx, pos // bs].astype(np.int64) * bs + pos % bs
+    with threadpool_limits(limits=cores):
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        t0 = time.perf_counter()
+        kp, vp = oracle.oracle_write(new_k[idx], new_v[idx], "bf16", slots, wl.k_pool, wl.v_pool, "bf16")
+        oracle.oracle_decode(wl.q[idx], "bf16", kp, vp, "bf16", wl.block_tables[idx],
+                             wl.context_lens[idx], wl.scale)
+        dt = time.perf_counter() - t0
+    kv = int(wl.context_lens[idx].astype(np.int64).sum()) * 2 * wl.num_kv_heads * wl.head_dim * 2
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(kv / dt / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(idx)} of {wl.num_seqs} sequences of the same batch, one step "
+                      f"(write + decode), float64 numpy; {dt:.2f}s",
+            "seconds": round(dt, 3), "host_cpus": cores, "cpu_model": cpu_model,
+            "decode_tokens_per_s_per_layer": round(len(idx) / dt, 3)}
+
+
+def calibrate_copy(mib, pa, torch, dev):
+    """pa_copy_blocks over MIB MiB of 64 KiB blocks (K and V 32 KiB each):
+    a plain copy of known size for scaling the HBM byte counters."""
+    import numpy as np
+    block_elems = 8 * 16 * 128
+    nblocks = max(2, (mib << 20) // (block_elems * 2 * 2))
+    k = torch.zeros((2 * nblocks, 8, 16, 128), dtype=torch.bfloat16, device=dev)
+    v = torch.zeros_like(k)
+    pool = pa.make_pool(k, v)
+    pairs = torch.from_numpy(np.stack([np.arange(nblocks), np.arange(nblocks, 2 * nblocks)], 1)
+                             .astype(np.int64)).to(dev)
+    for _ in range(3):
+        pa.pa_copy_blocks(pool, pairs)
+    torch.cuda.synchronize()
+    moved = nblocks * block_elems * 2 * 2
+    print(json.dumps({"calibration": "pa_copy_blocks", "bytes_read_per_launch": moved,
+                      "bytes_written_per_launch": moved, "launches": 3}), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -116,13 +116,15 @@ int pa_write_kv(const void *k, const void *v, int32_t src_dtype, int32_t num_tok
 
 /*
  * pa_decode_workspace_bytes -- device scratch pa_decode needs in split mode:
- * float32 partial maxima, sums and outputs for every (sequence, query head,
- * partition), with ceil(max_blocks_per_seq * block_size / partition_size)
- * partitions per sequence.  Returns 0 for partition_size == 0 (single pass)
- * and for invalid arguments.
+ * one int32 arrival counter per (sequence, group of up to 8 query heads
+ * sharing a KV head), padded to 256 bytes, then float32 partial maxima, sums
+ * and outputs for every (sequence, query head slot, partition), with
+ * ceil(max_blocks_per_seq * block_size / partition_size) partitions per
+ * sequence.  Returns 0 for partition_size == 0 (single pass) and for invalid
+ * arguments.
  */
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_blocks_per_seq, int32_t block_size,
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
                                  int32_t partition_size);
 
 /*
@@ -157,12 +159,16 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *   partition_size  0: single pass, one workgroup walks a whole context.
  *                 > 0: split-KV; a multiple of bs; partition p covers
  *                 positions [p*P, min((p+1)*P, n)); the partial results are
- *                 merged in increasing p by a second kernel on the same
- *                 stream.
+ *                 merged in increasing p, so the output does not depend on
+ *                 the order in which partitions finish.
  *   workspace     device scratch of at least pa_decode_workspace_bytes(...)
  *                 bytes when partition_size > 0 (else may be NULL).  Its
- *                 contents on entry do not matter.  Concurrent calls must not
- *                 share one workspace.
+ *                 leading bytes hold the arrival counters, which MUST be zero
+ *                 before the first call that uses the workspace: zero-fill
+ *                 the whole workspace once when it is allocated.  Every call
+ *                 leaves the counters zero again; the rest may hold
+ *                 anything.  Calls that may run concurrently must not share
+ *                 one workspace.
  */
 int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
               const pa_kv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,

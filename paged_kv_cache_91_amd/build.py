@@ -14,7 +14,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libpa.so")
-SOURCES = [os.path.join(PKG, "csrc", "pa_kernels.hip"), os.path.join(PKG, "csrc", "pa_api.cpp")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("pa_kernels.hip", "pa_decode_fast.hip", "pa_api.cpp")]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -81,6 +81,33 @@ int hip_fail(hipError_t e) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Query heads per workgroup: the group size rounded up to a power of two, at
+// most 8; larger groups are split into head groups of 8.
+int heads_per_wg(int group) {
+  int h = 1;
+  while (h < group && h < 8) h <<= 1;
+  return h;
+}
+
+// Split-KV scratch: one int32 arrival counter per (sequence, head group),
+// padded to 256 bytes, then float32 partials (m, l and head_dim outputs) for
+// every (sequence, head group, partition, head of the group).
+bool workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
+                      int32_t partition_size, pa_impl::WorkspaceLayout *w) {
+  if (partition_size <= 0 || num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads || head_dim <= 0 || max_blocks_per_seq <= 0 || block_size <= 0)
+    return false;
+  const int group = num_q_heads / num_kv_heads;
+  const int hpw = heads_per_wg(group);
+  const int64_t hg = ceil_div(group, hpw);
+  w->units = static_cast<int64_t>(num_seqs) * num_kv_heads * hg;
+  w->max_parts = ceil_div(static_cast<int64_t>(max_blocks_per_seq) * block_size, partition_size);
+  w->counter_bytes = ceil_div(w->units * 4, 256) * 256;
+  w->partial_floats = w->units * w->max_parts * hpw * (static_cast<int64_t>(head_dim) + 2);
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -134,15 +161,14 @@ int pa_write_kv(const void *k, const void *v, int32_t src_dtype, int32_t num_tok
   return ok();
 }
 
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_blocks_per_seq, int32_t block_size,
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
                                  int32_t partition_size) {
-  if (partition_size <= 0 || num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 ||
-      max_blocks_per_seq <= 0 || block_size <= 0)
+  pa_impl::WorkspaceLayout w{};
+  if (!workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                        block_size, partition_size, &w))
     return 0;
-  const int64_t parts = ceil_div(static_cast<int64_t>(max_blocks_per_seq) * block_size, partition_size);
-  const int64_t rows = static_cast<int64_t>(num_seqs) * num_q_heads * parts;
-  return static_cast<size_t>(rows) * (static_cast<size_t>(head_dim) + 2) * sizeof(float);
+  return static_cast<size_t>(w.total_bytes());
 }
 
 int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
@@ -174,8 +200,7 @@ int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
                 partition_size, pool->block_size);
 
   const int group = num_q_heads / pool->num_kv_heads;
-  int hpw = 1;
-  while (hpw < group && hpw < 8) hpw <<= 1;
+  const int hpw = heads_per_wg(group);
   const int head_groups = static_cast<int>(ceil_div(group, hpw));
   if (static_cast<int64_t>(pool->num_kv_heads) * head_groups > 65535)
     return fail(PA_ERR_INVALID_ARG, "too many heads");
@@ -205,24 +230,39 @@ int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * ks * log2e);
   a.v_scale = pool->dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
 
+  const bool fast = pa_impl::fast_decode_applies(q_dtype, pool->dtype, a);
   if (partition_size > 0) {
-    const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, pool->head_dim,
-                                                  max_blocks_per_seq, pool->block_size, partition_size);
+    pa_impl::WorkspaceLayout w{};
+    workspace_layout(num_seqs, num_q_heads, pool->num_kv_heads, pool->head_dim, max_blocks_per_seq,
+                     pool->block_size, partition_size, &w);
+    const size_t need = static_cast<size_t>(w.total_bytes());
     if (!workspace || workspace_bytes < need)
       return fail(PA_ERR_WORKSPACE, "split-KV workspace needs %zu bytes, got %zu", need,
                   workspace ? workspace_bytes : static_cast<size_t>(0));
-    const int64_t parts = ceil_div(static_cast<int64_t>(max_blocks_per_seq) * pool->block_size, partition_size);
-    a.max_parts = static_cast<int32_t>(parts);
-    const int64_t rows = static_cast<int64_t>(num_seqs) * num_q_heads * parts;
-    float *ws = static_cast<float *>(workspace);
-    a.part_m = ws;
-    a.part_l = ws + rows;
-    a.part_o = ws + 2 * rows;
+    a.max_parts = static_cast<int32_t>(w.max_parts);
+    a.counters = static_cast<int32_t *>(workspace);
+    float *ws = reinterpret_cast<float *>(static_cast<char *>(workspace) + w.counter_bytes);
+    if (fast) {
+      // [unit][part][head][D] outputs, then [unit][part][head][m, l]
+      a.part_o = ws;
+      a.part_m = ws + w.units * w.max_parts * hpw * pool->head_dim;
+      a.part_l = nullptr;
+    } else {
+      // [S][Hq][part] maxima, [S][Hq][part] sums, [S][Hq][part][D] outputs
+      const int64_t rows = static_cast<int64_t>(num_seqs) * num_q_heads * w.max_parts;
+      a.part_m = ws;
+      a.part_l = ws + rows;
+      a.part_o = ws + 2 * rows;
+    }
   }
-  bool supported = true;
-  hipError_t e = pa_impl::launch_decode(q_dtype, pool->dtype, a, reinterpret_cast<hipStream_t>(stream),
-                                        &supported);
-  if (!supported) return fail(PA_ERR_UNSUPPORTED, "decode specialisation not built");
+  hipError_t e;
+  if (fast) {
+    e = pa_impl::launch_decode_fast(q_dtype, pool->dtype, a, reinterpret_cast<hipStream_t>(stream));
+  } else {
+    bool supported = true;
+    e = pa_impl::launch_decode(q_dtype, pool->dtype, a, reinterpret_cast<hipStream_t>(stream), &supported);
+    if (!supported) return fail(PA_ERR_UNSUPPORTED, "decode specialisation not built");
+  }
   if (e != hipSuccess) return hip_fail(e);
   return ok();
 }

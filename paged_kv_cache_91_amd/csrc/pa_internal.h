@@ -20,6 +20,7 @@ struct DecodeArgs {
   float *part_m;           // split mode: [S][Hq][max_parts]
   float *part_l;           // split mode: [S][Hq][max_parts]
   float *part_o;           // split mode: [S][Hq][max_parts][D]
+  int32_t *counters;       // split mode: arrivals per (sequence, head group); zero between calls
   int64_t num_blocks;
   int32_t num_seqs;
   int32_t num_q_heads;
@@ -68,5 +69,19 @@ hipError_t launch_decode(int q_dtype, int kv_dtype, const DecodeArgs &a, hipStre
 hipError_t launch_write(int src_dtype, int dst_dtype, const WriteArgs &a, hipStream_t s,
                         bool *supported);
 hipError_t launch_copy(const CopyArgs &a, hipStream_t s);
+
+// head_dim 128 decode with matrix-core q.K^T and the fused split merge
+// (pa_decode_fast.hip); fast_decode_applies() says whether it covers a call.
+bool fast_decode_applies(int q_dtype, int kv_dtype, const DecodeArgs &a);
+hipError_t launch_decode_fast(int q_dtype, int kv_dtype, const DecodeArgs &a, hipStream_t s);
+
+// Workspace layout shared by the API layer and the kernels.
+struct WorkspaceLayout {
+  int64_t units;           // S * Hkv * head_groups
+  int64_t max_parts;
+  int64_t counter_bytes;   // int32 per unit, rounded up to 256 bytes
+  int64_t partial_floats;  // units * max_parts * heads_per_wg * (head_dim + 2)
+  int64_t total_bytes() const { return counter_bytes + partial_floats * 4; }
+};
 
 }  // namespace pa_impl

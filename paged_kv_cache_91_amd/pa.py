@@ -71,7 +71,7 @@ def lib() -> ctypes.CDLL:
         pool_p = ctypes.POINTER(KvPool)
         L.pa_write_kv.argtypes = [vp, vp, i32, i32, vp, pool_p, vp]
         L.pa_write_kv.restype = ctypes.c_int
-        L.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.pa_decode_workspace_bytes.restype = ctypes.c_size_t
         L.pa_decode.argtypes = [vp, i32, i32, i32, pool_p, vp, i32, vp, ctypes.c_float, vp, i32,
                                 vp, ctypes.c_size_t, vp]
@@ -155,10 +155,19 @@ def pa_write_kv(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, po
            "pa_write_kv")
 
 
-def pa_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
+def pa_decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                               max_blocks_per_seq: int, block_size: int, partition_size: int) -> int:
-    return int(lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
-                                               block_size, partition_size))
+    return int(lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                               max_blocks_per_seq, block_size, partition_size))
+
+
+def new_workspace(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                  max_blocks_per_seq: int, block_size: int, partition_size: int,
+                  device="cuda") -> torch.Tensor:
+    """Zero-filled split-KV workspace (its arrival counters must start at zero)."""
+    n = pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                                  block_size, partition_size)
+    return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
 
 
 def pa_decode(q: torch.Tensor, pool: KvPool, block_tables: torch.Tensor,
@@ -167,8 +176,8 @@ def pa_decode(q: torch.Tensor, pool: KvPool, block_tables: torch.Tensor,
               q_dtype: Optional[str] = None, stream=None) -> torch.Tensor:
     """Paged decode attention; returns ``out`` ([S, Hq, D], q's dtype).
 
-    ``workspace`` (split mode) is allocated here when not given; pass one in
-    to keep allocation out of a timed loop.
+    ``workspace`` (split mode) is allocated zero-filled here when not given;
+    pass one from :func:`new_workspace` to keep allocation out of a timed loop.
     """
     if q.dim() != 3:
         raise ValueError("q must be [num_seqs, num_q_heads, head_dim]")
@@ -185,9 +194,9 @@ def pa_decode(q: torch.Tensor, pool: KvPool, block_tables: torch.Tensor,
     maxb = int(block_tables.shape[1])
     ws_ptr, ws_bytes = None, 0
     if partition_size > 0:
-        need = pa_decode_workspace_bytes(s, hq, d, maxb, pool.block_size, partition_size)
         if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = new_workspace(s, hq, pool.num_kv_heads, d, maxb, pool.block_size,
+                                      partition_size, device=q.device)
         ws_ptr, ws_bytes = _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size()
     _check(lib().pa_decode(_ptr(q, "q"), qcode, s, hq, ctypes.byref(pool), _ptr(block_tables, "block_tables"),
                            maxb, _ptr(context_lens, "context_lens"), float(scale), _ptr(out, "out"),

@@ -391,9 +391,12 @@ def build_write_filled(seed: int, *, name: str, q_dtype: str, src_dtype: str, kv
         k_scale = float(np.float32(np.abs(widen(k_rows)).max()) / np.float32(448.0))
         v_scale = float(np.float32(np.abs(widen(v_rows)).max()) / np.float32(448.0))
     shape = (num_blocks, hkv, block_size, d)
-    fill = NAN_BITS[kv_dtype] if poison else STORAGE[kv_dtype](0)
-    k_pool = np.full(shape, fill, dtype=STORAGE[kv_dtype])
-    v_pool = np.full(shape, fill, dtype=STORAGE[kv_dtype])
+    if poison:
+        k_pool = np.full(shape, NAN_BITS[kv_dtype], dtype=STORAGE[kv_dtype])
+        v_pool = np.full(shape, NAN_BITS[kv_dtype], dtype=STORAGE[kv_dtype])
+    else:
+        k_pool = np.zeros(shape, dtype=STORAGE[kv_dtype])
+        v_pool = np.zeros(shape, dtype=STORAGE[kv_dtype])
     q = cast_f32(normal_f32(seed, _S_Q, len(lens) * num_q_heads * d), q_dtype).reshape(
         len(lens), num_q_heads, d)
     return Workload(
@@ -403,7 +406,8 @@ def build_write_filled(seed: int, *, name: str, q_dtype: str, src_dtype: str, kv
         scale=float(np.float32(1.0 / math.sqrt(d))), k_scale=k_scale, v_scale=v_scale,
         partition_size=partition_size, write_src_dtype=src_dtype, write_k=k_rows,
         write_v=v_rows, slot_mapping=slot_mapping,
-        meta={"seed": seed, "alloc": alloc.stats(), "poison": poison, "pad_block": pad})
+        meta={"seed": seed, "alloc": alloc.stats(), "poison": poison, "pad_block": pad,
+              "filled_by_write": True})
 
 
 def config5(seed: int = 5, num_seqs: int = 32, ctx_range=(8192, 32768),

@@ -39,11 +39,16 @@ def test_status_strings_and_version():
 
 
 def test_workspace_bytes():
-    # rows = S * Hq * ceil(maxb * bs / P); each row holds m, l and D outputs
-    assert pa.pa_decode_workspace_bytes(32, 64, 128, 1024, 32, 512) == 32 * 64 * 64 * 130 * 4
-    assert pa.pa_decode_workspace_bytes(3, 2, 8, 5, 4, 8) == 3 * 2 * 3 * 10 * 4
-    assert pa.pa_decode_workspace_bytes(3, 2, 8, 5, 4, 0) == 0
-    assert pa.pa_decode_workspace_bytes(0, 2, 8, 5, 4, 8) == 0
+    # counters: one int32 per (sequence, head group), padded to 256 bytes;
+    # partials: per (sequence, head group, partition, head slot) m, l and D outputs
+    assert pa.pa_decode_workspace_bytes(32, 64, 8, 128, 1024, 32, 512) == 1024 + 32 * 8 * 64 * 8 * 130 * 4
+    assert pa.pa_decode_workspace_bytes(3, 2, 1, 8, 5, 4, 8) == 256 + 3 * 3 * 2 * 10 * 4
+    # group 3 is handled as 4 head slots; group 16 as two head groups of 8
+    assert pa.pa_decode_workspace_bytes(2, 12, 4, 64, 4, 16, 32) == 256 + 2 * 4 * 2 * 4 * 66 * 4
+    assert pa.pa_decode_workspace_bytes(100, 32, 2, 64, 1, 16, 16) == 1792 + 100 * 2 * 2 * 1 * 8 * 66 * 4
+    assert pa.pa_decode_workspace_bytes(3, 2, 1, 8, 5, 4, 0) == 0
+    assert pa.pa_decode_workspace_bytes(0, 2, 1, 8, 5, 4, 8) == 0
+    assert pa.pa_decode_workspace_bytes(3, 3, 2, 8, 5, 4, 8) == 0      # heads not a multiple
 
 
 def _pool(**kw):

@@ -115,3 +115,28 @@ def test_poison_layout():
             assert (wl.k_pool[wl.block_tables[s, nb - 1], :, n % 16:, :] == W.NAN_BITS["bf16"]).all()
         g = oracle.gather_kv(wl.k_pool, wl.block_tables[s], int(n))
         assert not np.isnan(oracle.to_float64(g, "bf16")).any()
+
+
+def test_subset_relabelling_keeps_oracle_results():
+    """The GPU tests compare sampled sequences through a compacted copy of
+    their blocks; that copy must leave the oracle's results bit-identical."""
+    from gpu_util import subset
+
+    wl = W.config2(seed=51, num_seqs=6, ctx_range=(1, 300), num_blocks=256)
+    full = oracle.oracle_decode(wl.q, "bf16", wl.k_pool, wl.v_pool, "bf16", wl.block_tables,
+                                wl.context_lens, wl.scale)
+    sub = subset(wl, [4, 1])
+    got = oracle.oracle_decode(sub.q, "bf16", sub.k_pool, sub.v_pool, "bf16", sub.block_tables,
+                               sub.context_lens, sub.scale)
+    assert np.array_equal(got, full[[4, 1]])
+    wl5 = W.config5(num_seqs=3, ctx_range=(40, 200), num_blocks=64)
+    kp, vp = oracle.oracle_write(wl5.write_k, wl5.write_v, "bf16", wl5.slot_mapping, wl5.k_pool,
+                                 wl5.v_pool, "fp8_e4m3", wl5.k_scale, wl5.v_scale)
+    full = oracle.oracle_decode(wl5.q, "bf16", kp, vp, "fp8_e4m3", wl5.block_tables,
+                                wl5.context_lens, wl5.scale, wl5.k_scale, wl5.v_scale)
+    sub = subset(wl5, [2])
+    kp, vp = oracle.oracle_write(sub.write_k, sub.write_v, "bf16", sub.slot_mapping, sub.k_pool,
+                                 sub.v_pool, "fp8_e4m3", sub.k_scale, sub.v_scale)
+    got = oracle.oracle_decode(sub.q, "bf16", kp, vp, "fp8_e4m3", sub.block_tables,
+                               sub.context_lens, sub.scale, sub.k_scale, sub.v_scale)
+    assert np.array_equal(got, full[[2]])
