@@ -50,8 +50,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--layers", type=int, default=8, help="independent layer pools to rotate over")
-    ap.add_argument("--partition", type=int, default=1024,
-                    help="split-KV partition size in tokens (0 = single pass)")
+    ap.add_argument("--partition", type=int, default=-1,
+                    help="split-KV partition size in tokens (0 = single pass, -1 = balanced split)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=64,
                     help="sequences of the batch the oracle baseline processes")

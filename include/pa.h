@@ -79,6 +79,10 @@ typedef enum {
   PA_ERR_HIP = -4          /* the HIP runtime refused the launch */
 } pa_status;
 
+/* partition_size value asking pa_decode to balance the work itself (see
+ * pa_decode). */
+#define PA_PARTITION_AUTO (-1)
+
 /* Describes a caller-owned K/V pool pair. */
 typedef struct {
   void *k_pool;          /* device, [num_blocks][num_kv_heads][block_size][head_dim] */
@@ -118,10 +122,13 @@ int pa_write_kv(const void *k, const void *v, int32_t src_dtype, int32_t num_tok
  * pa_decode_workspace_bytes -- device scratch pa_decode needs in split mode:
  * one int32 arrival counter per (sequence, group of up to 8 query heads
  * sharing a KV head), padded to 256 bytes, then float32 partial maxima, sums
- * and outputs for every (sequence, query head slot, partition), with
+ * and outputs.  With partition_size > 0 there is a partial for every
+ * (sequence, query head slot, partition), with
  * ceil(max_blocks_per_seq * block_size / partition_size) partitions per
- * sequence.  Returns 0 for partition_size == 0 (single pass) and for invalid
- * arguments.
+ * sequence.  With PA_PARTITION_AUTO there are two partials per workgroup the
+ * balanced split may launch, 16 per compute unit of the CURRENT device, so
+ * size the workspace with the device that will run the call selected.
+ * Returns 0 for partition_size == 0 (single pass) and for invalid arguments.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
@@ -156,7 +163,15 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *   scale         softmax scale (typically 1/sqrt(head_dim)); finite.
  *   out           device, [num_seqs][num_q_heads][head_dim] of q_dtype,
  *                 rounded to nearest even from float32.  Must not overlap q.
- *   partition_size  0: single pass, one workgroup walks a whole context.
+ *   partition_size  PA_PARTITION_AUTO (-1): the library balances the work.
+ *                 For head_dim 128 at block size 16 or 32 every launched
+ *                 wave gets an equal share of the batch's 16-position tiles
+ *                 (a context may be cut anywhere on a tile boundary, and the
+ *                 pieces are merged in context order); the cut points depend
+ *                 on the batch's lengths and the GPU's size, so results are
+ *                 bit-identical across runs and block relabellings on one
+ *                 GPU model.  Other shapes run single pass.
+ *                 0: single pass, one workgroup walks a whole context.
  *                 > 0: split-KV; a multiple of bs; partition p covers
  *                 positions [p*P, min((p+1)*P, n)); the partial results are
  *                 merged in increasing p, so the output does not depend on

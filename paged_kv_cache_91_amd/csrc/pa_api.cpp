@@ -95,16 +95,25 @@ int heads_per_wg(int group) {
 bool workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                       int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
                       int32_t partition_size, pa_impl::WorkspaceLayout *w) {
-  if (partition_size <= 0 || num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
-      num_q_heads % num_kv_heads || head_dim <= 0 || max_blocks_per_seq <= 0 || block_size <= 0)
+  if ((partition_size <= 0 && partition_size != PA_PARTITION_AUTO) || num_seqs <= 0 ||
+      num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads || head_dim <= 0 ||
+      max_blocks_per_seq <= 0 || block_size <= 0)
     return false;
   const int group = num_q_heads / num_kv_heads;
   const int hpw = heads_per_wg(group);
   const int64_t hg = ceil_div(group, hpw);
   w->units = static_cast<int64_t>(num_seqs) * num_kv_heads * hg;
-  w->max_parts = ceil_div(static_cast<int64_t>(max_blocks_per_seq) * block_size, partition_size);
   w->counter_bytes = ceil_div(w->units * 4, 256) * 256;
-  w->partial_floats = w->units * w->max_parts * hpw * (static_cast<int64_t>(head_dim) + 2);
+  if (partition_size == PA_PARTITION_AUTO) {
+    // balanced split: at most two partials per launched wave
+    w->stream_waves = static_cast<int64_t>(pa_impl::device_compute_units()) * pa_impl::kMaxStreamWavesPerCu;
+    w->max_parts = 0;
+    w->partial_floats = w->stream_waves * 2 * hpw * (static_cast<int64_t>(head_dim) + 2);
+  } else {
+    w->stream_waves = 0;
+    w->max_parts = ceil_div(static_cast<int64_t>(max_blocks_per_seq) * block_size, partition_size);
+    w->partial_floats = w->units * w->max_parts * hpw * (static_cast<int64_t>(head_dim) + 2);
+  }
   return true;
 }
 
@@ -194,7 +203,8 @@ int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
   const bool combo = (q_dtype == pool->dtype) ||
                      (pool->dtype == PA_FP8_E4M3 && (q_dtype == PA_BF16 || q_dtype == PA_F16));
   if (!combo) return fail(PA_ERR_UNSUPPORTED, "q dtype %d with pool dtype %d not built", q_dtype, pool->dtype);
-  if (partition_size < 0) return fail(PA_ERR_INVALID_ARG, "partition_size must be >= 0");
+  if (partition_size < 0 && partition_size != PA_PARTITION_AUTO)
+    return fail(PA_ERR_INVALID_ARG, "partition_size must be >= 0 or PA_PARTITION_AUTO");
   if (partition_size > 0 && partition_size % pool->block_size)
     return fail(PA_ERR_INVALID_ARG, "partition_size %d is not a multiple of block_size %d",
                 partition_size, pool->block_size);
@@ -231,7 +241,25 @@ int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
   a.v_scale = pool->dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
 
   const bool fast = pa_impl::fast_decode_applies(q_dtype, pool->dtype, a);
-  if (partition_size > 0) {
+  if (partition_size == PA_PARTITION_AUTO && !fast) {
+    partition_size = 0;                 // the generic kernel walks each context in one pass
+    a.partition_size = 0;
+  }
+  if (partition_size == PA_PARTITION_AUTO) {
+    pa_impl::WorkspaceLayout w{};
+    workspace_layout(num_seqs, num_q_heads, pool->num_kv_heads, pool->head_dim, max_blocks_per_seq,
+                     pool->block_size, partition_size, &w);
+    const size_t need = static_cast<size_t>(w.total_bytes());
+    if (!workspace || workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "balanced-split workspace needs %zu bytes, got %zu", need,
+                  workspace ? workspace_bytes : static_cast<size_t>(0));
+    a.partition_size = 0;
+    a.stream_waves = static_cast<int32_t>(w.stream_waves);
+    a.counters = static_cast<int32_t *>(workspace);
+    float *ws = reinterpret_cast<float *>(static_cast<char *>(workspace) + w.counter_bytes);
+    a.part_o = ws;                                                  // [wave][2][head][D]
+    a.part_m = ws + w.stream_waves * 2 * hpw * pool->head_dim;      // [wave][2][head][m, l]
+  } else if (partition_size > 0) {
     pa_impl::WorkspaceLayout w{};
     workspace_layout(num_seqs, num_q_heads, pool->num_kv_heads, pool->head_dim, max_blocks_per_seq,
                      pool->block_size, partition_size, &w);

@@ -33,6 +33,7 @@ struct DecodeArgs {
   int32_t bs_log2;
   int32_t max_blocks;
   int32_t partition_size;  // 0 = single pass
+  int32_t stream_waves;    // > 0: balanced (stream-K) split over this many single-wave workgroups
   int32_t max_parts;       // partitions per sequence in the workspace (1 if single pass)
   float scale_log2;        // scale * k_scale * log2(e)
   float v_scale;           // 1 unless fp8
@@ -75,10 +76,25 @@ hipError_t launch_copy(const CopyArgs &a, hipStream_t s);
 bool fast_decode_applies(int q_dtype, int kv_dtype, const DecodeArgs &a);
 hipError_t launch_decode_fast(int q_dtype, int kv_dtype, const DecodeArgs &a, hipStream_t s);
 
+// Compute units of the current device (256 when it cannot be queried, e.g.
+// on a machine without a GPU, where only sizes are computed).
+inline int device_compute_units() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;
+  return cus;
+}
+
+// Upper bound on resident single-wave workgroups per compute unit that the
+// balanced split may launch (its workspace is sized for this many).
+constexpr int kMaxStreamWavesPerCu = 16;
+
 // Workspace layout shared by the API layer and the kernels.
 struct WorkspaceLayout {
   int64_t units;           // S * Hkv * head_groups
-  int64_t max_parts;
+  int64_t max_parts;       // fixed partitions per sequence (0 in the balanced split)
+  int64_t stream_waves;    // balanced split: workgroups the partials are sized for
   int64_t counter_bytes;   // int32 per unit, rounded up to 256 bytes
   int64_t partial_floats;  // units * max_parts * heads_per_wg * (head_dim + 2)
   int64_t total_bytes() const { return counter_bytes + partial_floats * 4; }

@@ -20,6 +20,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
+PA_PARTITION_AUTO = -1          # pa_decode balances the split itself
 DTYPE_CODE = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "fp8_e4m3": PA_FP8_E4M3}
 _TORCH_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
                torch.float8_e4m3fn: PA_FP8_E4M3}
@@ -193,7 +194,7 @@ def pa_decode(q: torch.Tensor, pool: KvPool, block_tables: torch.Tensor,
     qcode = dtype_code(q, q_dtype)
     maxb = int(block_tables.shape[1])
     ws_ptr, ws_bytes = None, 0
-    if partition_size > 0:
+    if partition_size != 0:
         if workspace is None:
             workspace = new_workspace(s, hq, pool.num_kv_heads, d, maxb, pool.block_size,
                                       partition_size, device=q.device)

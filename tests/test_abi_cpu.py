@@ -49,6 +49,11 @@ def test_workspace_bytes():
     assert pa.pa_decode_workspace_bytes(3, 2, 1, 8, 5, 4, 0) == 0
     assert pa.pa_decode_workspace_bytes(0, 2, 1, 8, 5, 4, 8) == 0
     assert pa.pa_decode_workspace_bytes(3, 3, 2, 8, 5, 4, 8) == 0      # heads not a multiple
+    # balanced split: two partials per wave, 16 waves per compute unit (256 CUs
+    # assumed when no GPU can be queried, as here)
+    assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 128, 16, pa.PA_PARTITION_AUTO) == \
+        2048 + 256 * 16 * 2 * 4 * 130 * 4
+    assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 128, 16, -2) == 0
 
 
 def _pool(**kw):
@@ -100,6 +105,7 @@ def test_decode_rejects_bad_pool(pool_kw, expect):
     (dict(q_dtype=pa.PA_F16), -2),                 # f16 q with a bf16 pool
     (dict(part=24), -1),                           # not a multiple of block_size
     (dict(part=-16), -1),
+    (dict(part=-1), -3),                           # balanced split needs a workspace
     (dict(part=32), -3),                           # no workspace
     (dict(part=32, ws=FAKE * 7, ws_bytes=16), -3), # too small
 ])

@@ -16,7 +16,9 @@ from gpu_util import DEV, DeviceWorkload, dev_to_host, max_err, out_f64, say, su
 
 pytestmark = pytest.mark.gpu
 
-BENCH_PARTITION = 256
+from paged_kv_cache_91_amd.pa import PA_PARTITION_AUTO
+
+BENCH_PARTITION = PA_PARTITION_AUTO
 
 
 def sample_seqs(wl, k=6, seed=0):
@@ -57,7 +59,7 @@ def test_llama3_layer_full():
     dev = DeviceWorkload(wl, sparse=True)
     seqs = sample_seqs(wl, k=8)
     outs = {}
-    for p in (BENCH_PARTITION, 0, 512):
+    for p in (BENCH_PARTITION, 0, 512, 1024):
         got = out_f64(dev.decode(partition_size=p))
         assert np.isfinite(got).all()
         say(f"  partition {p}")
@@ -83,7 +85,7 @@ def test_mha_13b_full_with_write():
     dev = DeviceWorkload(wl, sparse=True)
     dev.write()
     seqs = sample_seqs(wl, k=6, seed=3)
-    for p in (0, 256):
+    for p in (0, 256, PA_PARTITION_AUTO):
         got = out_f64(dev.decode(partition_size=p))
         assert np.isfinite(got).all()
         say(f"  partition {p}")
@@ -104,7 +106,7 @@ def test_prefix_cow_full():
     before = out_f64(dev.decode())
     dev.copy()
     dev.set_tables(wl.block_tables)
-    for p in (0, 64):
+    for p in (0, 64, PA_PARTITION_AUTO):
         after = out_f64(dev.decode(partition_size=p))
         if p == 0:
             assert np.array_equal(before, after)
@@ -124,7 +126,7 @@ def test_long_context_fp8_split_full():
     dev = DeviceWorkload(wl, sparse=True)
     dev.write()
     seqs = sample_seqs(wl, k=2, seed=5)
-    for p in (wl.partition_size, 0):
+    for p in (wl.partition_size, 0, PA_PARTITION_AUTO):
         got = out_f64(dev.decode(partition_size=p))
         assert np.isfinite(got).all()
         say(f"  partition {p}")

@@ -61,7 +61,7 @@ def check_decode(wl, parts=(0,), label=""):
 
 def test_tiny_fp32():
     wl = W.config1()
-    check_decode(wl, parts=(0, 4, 8))
+    check_decode(wl, parts=(0, 4, 8, pa.PA_PARTITION_AUTO))
     pinned = W.config1()
     pinned.block_tables = np.array([[7, 2], [9, 0]], dtype=np.int32)   # zerocoder.ru example tables
     check_decode(pinned, parts=(0, 4), label="tables [7,2],[9]")
@@ -114,7 +114,7 @@ def test_decode_shapes(shape):
     wl = W.build_decode(100 + d, name=f"shape-{qd}", q_dtype=qd, kv_dtype=kd, num_q_heads=hq,
                         num_kv_heads=hkv, head_dim=d, block_size=bs, num_blocks=need + 7,
                         context_lens=lens, rng=rng)
-    check_decode(wl, parts=(0, bs, 4 * bs, 512 if 512 % bs == 0 else 8 * bs))
+    check_decode(wl, parts=(0, bs, 4 * bs, 512 if 512 % bs == 0 else 8 * bs, pa.PA_PARTITION_AUTO))
 
 
 FP8_SHAPES = [
@@ -134,7 +134,7 @@ def test_decode_fp8_cache(shape):
     wl = W.build_write_filled(200 + d, name="fp8", q_dtype=qd, src_dtype=src, kv_dtype="fp8_e4m3",
                               num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs,
                               num_blocks=need + 5, context_lens=lens, rng=rng)
-    check_decode(wl, parts=(0, bs, 4 * bs, 512 if 512 % bs == 0 else 8 * bs))
+    check_decode(wl, parts=(0, bs, 4 * bs, 512 if 512 % bs == 0 else 8 * bs, pa.PA_PARTITION_AUTO))
 
 
 def test_fp8_decode_every_code():
@@ -247,7 +247,7 @@ def test_relabelled_blocks_give_identical_bits():
     wl = W.config2(seed=21, num_seqs=6, ctx_range=(1, 600), num_blocks=512)
     other = W.relocate(wl, seed=22)
     a, b = DeviceWorkload(wl), DeviceWorkload(other)
-    for p in (0, 16, 64, 512):
+    for p in (0, 16, 64, 512, pa.PA_PARTITION_AUTO):
         x = a.decode(partition_size=p).cpu()
         y = b.decode(partition_size=p).cpu()
         assert torch.equal(x.view(torch.int16), y.view(torch.int16)), p
@@ -256,7 +256,7 @@ def test_relabelled_blocks_give_identical_bits():
 def test_deterministic_repeats():
     wl = W.config2(seed=23, num_seqs=5, ctx_range=(100, 900), num_blocks=512)
     dev = DeviceWorkload(wl)
-    for p in (0, 128):
+    for p in (0, 128, pa.PA_PARTITION_AUTO):
         x = dev.decode(partition_size=p).cpu()
         for _ in range(3):
             assert torch.equal(x.view(torch.int16), dev.decode(partition_size=p).cpu().view(torch.int16))
@@ -275,7 +275,8 @@ def test_poisoned_unused_memory_is_never_used(which):
     else:
         wl = W.config3(seed=33, num_seqs=5, num_blocks=256, length_cap=120, poison=True)
         wl.write_k = wl.write_v = wl.slot_mapping = None        # decode only
-    outs = check_decode(wl, parts=(0, wl.block_size, 512 if 512 % wl.block_size == 0 else 0))
+    outs = check_decode(wl, parts=(0, wl.block_size, 512 if 512 % wl.block_size == 0 else 0,
+                                   pa.PA_PARTITION_AUTO))
     for o in outs:
         assert np.isfinite(o).all()
 
@@ -288,7 +289,7 @@ def test_edge_lengths():
     wl = W.build_decode(41, name="edges", q_dtype="bf16", kv_dtype="bf16", num_q_heads=8,
                         num_kv_heads=2, head_dim=128, block_size=bs, num_blocks=need + 2,
                         context_lens=lens, rng=rng, max_blocks_per_seq=maxb)
-    outs = check_decode(wl, parts=(0, 16, 32))
+    outs = check_decode(wl, parts=(0, 16, 32, pa.PA_PARTITION_AUTO))
     for o in outs:
         assert not o[0].any() and not o[5].any()          # n == 0: zero rows
 
@@ -305,7 +306,7 @@ def test_out_of_range_table_entry_and_length_give_nan_rows():
     dev = DeviceWorkload(wl, tables=tables)
     dev.ctx = torch.from_numpy(lens).to(DEV)
     ref = oracle_out(wl)
-    for p in (0, 32):
+    for p in (0, 32, pa.PA_PARTITION_AUTO):
         got = out_f64(dev.decode(partition_size=p))
         assert np.isnan(got[1]).all() and np.isnan(got[2]).all()
         assert max_err(got[[0, 3]], ref[[0, 3]]) <= 2e-2
