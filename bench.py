@@ -10,7 +10,8 @@ One step = the whole hot path for one layer of one decode iteration:
   1. pa_write_kv  -- the newest token's K/V row of every sequence is written
                      through the slot mapping (position n-1);
   2. pa_decode    -- paged attention of every sequence over its n positions
-                     (split-KV with the log-sum-exp merge when --partition > 0).
+                     (split over the context with the log-sum-exp merge unless
+                     --partition is 0; the default -1 balances the split).
 Steps rotate over --layers independent pools (distinct device memory, each
 its own block permutation), as consecutive layers of a model would, so the
 K/V reads come from HBM rather than from the 256 MB last-level cache.
@@ -143,7 +144,7 @@ def main():
             tables=torch.from_numpy(tables).to(dev), slots=torch.from_numpy(slots).to(dev)))
     maxb = wl.max_blocks_per_seq
     ws = None
-    if args.partition > 0:
+    if args.partition != 0:
         ws = pa.new_workspace(S, wl.num_q_heads, hkv, d, maxb, bs, args.partition, device=dev)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
