@@ -27,6 +27,10 @@ FLAGS = [
     "-Wno-unused-function",
     # keep packed-fp32 instructions out of the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: left to its heuristics the compiler
+    # adds accumulation registers on top of ~200 VGPRs, which halves how many
+    # decode waves a SIMD holds
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I" + os.path.join(ROOT, "include"),
     "-I" + os.path.join(PKG, "csrc"),
 ]

@@ -1,6 +1,6 @@
-// Paged decode for head_dim 128 on gfx950: one wave per (partition, KV head
-// group, sequence), q.K^T on the matrix cores, P.V on the vector ALUs, and
-// the split-KV log-sum-exp merge done by the last partition to finish.
+// Paged decode for head_dim 128 on gfx950: q.K^T and P.V on the matrix
+// cores, the online softmax on the vector ALUs, and the split-KV log-sum-exp
+// merge done by the last piece of a context to finish.
 //
 // What is computed is the decode attention of gufacode.com "PagedAttention:KV
 // cache 的页表革命", section "PagedAttention CUDA Kernel" (per sequence: the
@@ -26,11 +26,16 @@
 // scale * log2 e).  Lane l holds the scores of positions 4*(l/16)+r, r < 4,
 // for head l%16.
 //
-// P.V on the VALU: lane l reads the V row of position 4*(l/16)+c (c < 4),
-// dims 8*(l%16)..+7, so every load instruction covers 4 whole rows; the
-// probability of that position for head h is broadcast inside the 16-lane
-// row from lane h (DPP row_newbcast).  The 4 row groups' partial sums are
-// added at the end.
+// P.V as eight 16x16x16 MFMAs per tile, one per e < 8: A = V restricted to
+// the dims 8*i+e (rows i < 16) over the tile's 16 positions, B = P (positions
+// x query heads), C[i][head] accumulating O[head][8*i+e] in fp32.  Lane l
+// reads the V rows of positions 4*(l/16)+c (c < 4), dims 8*(l%16)..+7, so
+// every load instruction covers 4 whole rows and the lane already holds its
+// A slots (4 positions of one dim) up to a 16-bit shuffle (v_perm); its B
+// slots (4 positions of head l%16) are exactly the probabilities the q.K^T
+// MFMA left in it, rounded to the MFMA's input type.  C lands with head l%16
+// and dims 32*(l/16)..+31 in lane l, so each lane's rescale factor is its own
+// head's and the outputs need no cross-lane sum.
 //
 // Split merge.  Each partition writes m, l and the unnormalised output o for
 // its heads, then bumps a per-(sequence, head group) counter; the partition
@@ -58,12 +63,26 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kHd = 128;      // head_dim handled here
 constexpr int kTile = 16;     // positions per MFMA tile
+constexpr int kDepth = 4;     // K/V tiles in flight per wave
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 template <typename QS> struct Mma;
 template <> struct Mma<BF16S> {
   using V8 = bf16x8_t;
+  using V4 = bf16x4_t;
   static __device__ __forceinline__ f32x4_t run(V8 a, V8 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t run16(V4 a, V4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+  // two floats -> two bf16 (round to nearest even) in one dword
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+    return __builtin_bit_cast(uint32_t, bf16x2_t{static_cast<__bf16>(x), static_cast<__bf16>(y)});
   }
   // two e4m3 codes (low or high half of w) -> two bf16 values, exact
   template <bool HI>
@@ -73,21 +92,21 @@ template <> struct Mma<BF16S> {
 };
 template <> struct Mma<F16S> {
   using V8 = f16x8_t;
+  using V4 = f16x4_t;
   static __device__ __forceinline__ f32x4_t run(V8 a, V8 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t run16(V4 a, V4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+    return __builtin_bit_cast(uint32_t, f16x2_t{static_cast<_Float16>(x), static_cast<_Float16>(y)});
   }
   template <bool HI>
   static __device__ __forceinline__ uint32_t from_fp8(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
   }
 };
-
-// Broadcast lane H of each 16-lane row to the whole row (DPP row_newbcast).
-template <int H>
-__device__ __forceinline__ float row_bcast(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + H,
-                                                            0xf, 0xf, true));
-}
 
 // Combine each lane's value with the lane 16 (resp. 32) away, on the VALU
 // (v_permlane16_swap / v_permlane32_swap), so no LDS traffic is involved.
@@ -176,18 +195,50 @@ __device__ __forceinline__ void fold(const Partial &x, float &big_m, float &l, f
   big_m = nm;
 }
 
+// Values every lane of the wave agrees on, marked as such for the compiler:
+// results of cross-lane reductions are otherwise treated as per-lane, which
+// turns loops over them into exec-masked loops with copied registers.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform(int64_t x) {
+  const uint64_t u = static_cast<uint64_t>(x);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-// K/V bytes are read exactly once: non-temporal loads keep them from
-// displacing reusable lines (tables, q, partials) in the caches.
-__device__ __forceinline__ uint4 load_stream(const uint8_t *p, uint4) {
-  const u32x4_t r = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
-  return make_uint4(r[0], r[1], r[2], r[3]);
+// K/V tiles are read with buffer loads: a tile is one (block, KV head)
+// range of 16 rows given as a buffer resource, so a load can be switched off
+// by giving the resource zero size (the instruction still issues and counts,
+// it reads nothing and returns zeros).  That keeps every step of the
+// prefetch ring unconditional, which the compiler's wait counting needs to
+// keep loads in flight across steps.  The loads are non-temporal: K/V bytes
+// are read exactly once and should not displace reusable lines.
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit elements (gfx9 family)
+constexpr int kLoadNt = 2;               // cache policy bits: non-temporal
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), 0, bytes, kRsrcWord3);
 }
-__device__ __forceinline__ uint2 load_stream(const uint8_t *p, uint2) {
-  const u32x2_t r = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
-  return make_uint2(r[0], r[1]);
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t r, int off, uint4 &x) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadNt);
+  x = make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t r, int off, uint2 &x) {
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kLoadNt);
+  x = make_uint2(v[0], v[1]);
+}
+
+// Block-table entries and context lengths are read through the constant
+// address space: they are not written while the kernel runs, and such loads
+// become scalar loads, whose completion is counted apart from the K/V loads
+// (a vector load of a table entry would wait behind the tile loads issued
+// before it).
+typedef const __attribute__((address_space(4))) int32_t cint32_t;
+__device__ __forceinline__ int load_const(const int32_t *p, int64_t i) {
+  return ((cint32_t *)p)[i];
 }
 
 // NW waves share one partition: wave w takes tiles w, w+NW, w+2NW, ...; the
@@ -214,20 +265,26 @@ struct Fast {
     VRaw v[4];
   };
 
+  // Issue the loads of the tile whose 16 rows start at byte `off` of the K
+  // and V pools (uniform), or loads that read nothing when !on.  ko / vo are
+  // this lane's byte offsets inside a tile (lane_offsets()).
   static __device__ __forceinline__ void issue(Tile &t, const uint8_t *__restrict__ kb,
-                                               const uint8_t *__restrict__ vb, int64_t off_blk,
-                                               int o0, int r16, int g4) {
-    const uint8_t *kp = kb + off_blk + (o0 + r16) * kRow;
-    if constexpr (kFp8) {
-      t.k[0] = load_stream(kp + 16 * g4, uint4{});
-      t.k[1] = load_stream(kp + 64 + 16 * g4, uint4{});
-    } else {
+                                               const uint8_t *__restrict__ vb, int64_t off, bool on,
+                                               int ko, int vo) {
+    const int bytes = on ? kTile * kRow : 0;
+    const auto rk = tile_rsrc(kb + off, bytes);
+    const auto rv = tile_rsrc(vb + off, bytes);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) t.k[j] = load_stream(kp + (32 * j + 8 * g4) * 2, uint4{});
-    }
-    const uint8_t *vp = vb + off_blk + (o0 + 4 * g4) * kRow + 8 * r16 * kEsz;
+    for (int j = 0; j < (kFp8 ? 2 : 4); ++j) load_tile(rk, ko + 64 * j, t.k[j]);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) t.v[c] = load_stream(vp + c * kRow, VRaw{});
+    for (int c = 0; c < 4; ++c) load_tile(rv, vo + c * kRow, t.v[c]);
+  }
+  // K: lane (r16, g4) reads row r16, 16 bytes at 16*g4 of every 64-byte
+  // chunk (the MFMA A slots, matching dbase); V: rows 4*g4 .. 4*g4+3, the
+  // 8 elements from 8*r16.
+  static __device__ __forceinline__ int k_lane_offset(int r16, int g4) { return r16 * kRow + 16 * g4; }
+  static __device__ __forceinline__ int v_lane_offset(int r16, int g4) {
+    return 4 * g4 * kRow + 8 * r16 * kEsz;
   }
 
   static __device__ __forceinline__ V8 a_operand(const Tile &t, int j) {
@@ -246,31 +303,66 @@ struct Fast {
     }
   }
 
-  static __device__ __forceinline__ void widen_v(const Tile &t, int c, float *f) {
+  // P.V for one tile: acc[e] += V(dims 8*i+e) x P, e < 8 (see the layout
+  // notes at the top).  v_perm builds the A operand from the lane's rows:
+  // selector 0x05040100 takes the low 16 bits of two dwords, 0x07060302 the
+  // high 16 bits.  fp8 rows are first transposed bytewise (four rows' codes
+  // of one dim into one dword) and then widened exactly to the MFMA type.
+  template <bool MASKED>
+  static __device__ __forceinline__ void pv(const Tile &t, const uint32_t pb_lo, const uint32_t pb_hi,
+                                            int p0, int pend, f32x4_t (&acc)[8]) {
+    using V4 = typename M::V4;
+    const V4 pb = __builtin_bit_cast(V4, make_uint2(pb_lo, pb_hi));
+    auto mma = [&](int e, uint32_t a01, uint32_t a23) {
+      acc[e] = M::run16(__builtin_bit_cast(V4, make_uint2(a01, a23)), pb, acc[e]);
+    };
+    // rows past the context end have p = 0, but their stale bytes may hold
+    // NaN or Inf, so they are zeroed before the product
+    auto keep = [&](int c) { return !MASKED || p0 + c < pend; };
     if constexpr (kFp8) {
-      Kv<FP8S>::widen(t.v[c], f);
+      uint32_t x[4][2];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        x[c][0] = keep(c) ? t.v[c].x : 0u;
+        x[c][1] = keep(c) ? t.v[c].y : 0u;
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t t01l = __builtin_amdgcn_perm(x[1][k], x[0][k], 0x05010400u);
+        const uint32_t t01h = __builtin_amdgcn_perm(x[1][k], x[0][k], 0x07030602u);
+        const uint32_t t23l = __builtin_amdgcn_perm(x[3][k], x[2][k], 0x05010400u);
+        const uint32_t t23h = __builtin_amdgcn_perm(x[3][k], x[2][k], 0x07030602u);
+        const uint32_t y[4] = {__builtin_amdgcn_perm(t23l, t01l, 0x05040100u),
+                               __builtin_amdgcn_perm(t23l, t01l, 0x07060302u),
+                               __builtin_amdgcn_perm(t23h, t01h, 0x05040100u),
+                               __builtin_amdgcn_perm(t23h, t01h, 0x07060302u)};
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          mma(4 * k + b, M::template from_fp8<false>(y[b]), M::template from_fp8<true>(y[b]));
+      }
     } else {
-      Kv<KS>::widen(t.v[c], f);
-    }
-  }
-
-  static __device__ __forceinline__ float bcast_head(float x, int h) {
-    switch (h) {
-      case 0: return row_bcast<0>(x);
-      case 1: return row_bcast<1>(x);
-      case 2: return row_bcast<2>(x);
-      case 3: return row_bcast<3>(x);
-      case 4: return row_bcast<4>(x);
-      case 5: return row_bcast<5>(x);
-      case 6: return row_bcast<6>(x);
-      default: return row_bcast<7>(x);
+      uint32_t x[4][4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        x[c][0] = keep(c) ? t.v[c].x : 0u;
+        x[c][1] = keep(c) ? t.v[c].y : 0u;
+        x[c][2] = keep(c) ? t.v[c].z : 0u;
+        x[c][3] = keep(c) ? t.v[c].w : 0u;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        mma(2 * k, __builtin_amdgcn_perm(x[1][k], x[0][k], 0x05040100u),
+            __builtin_amdgcn_perm(x[3][k], x[2][k], 0x05040100u));
+        mma(2 * k + 1, __builtin_amdgcn_perm(x[1][k], x[0][k], 0x07060302u),
+            __builtin_amdgcn_perm(x[3][k], x[2][k], 0x07060302u));
+      }
     }
   }
 
   template <bool MASKED>
   static __device__ __forceinline__ void compute(const Tile &t, const V8 (&qb)[4], int tpos,
-                                                 int pend, int r16, int g4, float scale_log2,
-                                                 float &m_run, float &l_run, float (&acc)[GT][8]) {
+                                                 int pend, int g4, float scale_log2,
+                                                 float &m_run, float &l_run, f32x4_t (&acc)[8]) {
     f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) s = M::run(a_operand(t, j), qb[j], s);
@@ -290,96 +382,72 @@ struct Fast {
     for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sc[r] - m_new);
     l_run = fmaf(l_run, alpha, (p[0] + p[1]) + (p[2] + p[3]));
     m_run = m_new;
-    // rescale the accumulators only when some head's maximum moved
+    // rescale the accumulators (this lane's head's) only when some head's
+    // maximum moved
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-      for (int h = 0; h < GT; ++h) {
-        const float ah = bcast_head(alpha, h);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= ah;
-      }
+      for (int e = 0; e < 8; ++e) acc[e] *= alpha;
     }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      float vf[8];
-      widen_v(t, c, vf);
-      if constexpr (MASKED) {
-        const bool ok = p0 + c < pend;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vf[e] = ok ? vf[e] : 0.0f;
-      }
-#pragma unroll
-      for (int h = 0; h < GT; ++h) {
-        const float ph = bcast_head(p[c], h);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
-      }
-    }
+    pv<MASKED>(t, M::pack2(p[0], p[1]), M::pack2(p[2], p[3]), p0, pend, acc);
   }
 
   // Accumulate `count` tiles of one (sequence, head group) into this wave's
   // online-softmax state: tile t_first + stride * i for i < count, each 16
   // positions starting at 16 * tile; positions >= pend are masked.
+  //
+  // The tiles stream through a ring of kDepth buffers: the loads of tile
+  // i + kDepth are issued as soon as tile i has been computed, so kDepth
+  // tiles are in flight while one is computed.  Every step issues loads
+  // (switched off past the last tile), and a scheduling barrier keeps each
+  // buffer's new loads after the compute that frees it, so the buffers stay
+  // in place and the waits stay exact.  Table entries are fetched one step
+  // ahead with scalar loads.
   static __device__ __forceinline__ void accumulate(
       const DecodeArgs &a, const V8 (&qb)[4], const uint8_t *__restrict__ kb,
       const uint8_t *__restrict__ vb, const int32_t *__restrict__ trow, int pend, int t_first,
-      int count, int stride, int r16, int g4, float &m_run, float &l_run, float (&acc)[GT][8],
+      int count, int stride, int r16, int g4, float &m_run, float &l_run, f32x4_t (&acc)[8],
       bool &bad) {
     const int64_t blk_bytes = static_cast<int64_t>(BS) * kRow * a.num_kv_heads;
     const int jmax = (pend - 1) / BS;
+    const int ko = k_lane_offset(r16, g4), vo = v_lane_offset(r16, g4);
     auto tpos = [&](int i) { return (t_first + stride * i) * kTile; };
-    auto lookup = [&](int i) -> int64_t {
-      const int j = min(tpos(i) / BS, jmax);
-      int64_t ph = trow[j];
-      if (static_cast<uint64_t>(ph) >= static_cast<uint64_t>(a.num_blocks)) {
-        bad = true;
-        ph = 0;
-      }
-      return ph * blk_bytes;
+    // raw table entry for tile i (clamped to the last block, so always readable)
+    auto entry = [&](int i) { return load_const(trow, min(tpos(i) / BS, jmax)); };
+    // issue tile i from table entry e (nothing when i >= count or e is bad)
+    auto issue_tile = [&](Tile &t, int i, int e) {
+      const bool valid = static_cast<uint32_t>(e) < static_cast<uint32_t>(a.num_blocks);
+      const bool live = i < count;
+      bad |= live && !valid;
+      const int64_t off = (valid ? static_cast<int64_t>(e) * blk_bytes : 0) + tpos(i) % BS * kRow;
+      issue(t, kb, vb, off, live && valid, ko, vo);
     };
-    auto in_block = [&](int i) { return min(tpos(i), pend - 1) % BS / kTile * kTile; };
 
     m_run = -INFINITY;
     l_run = 0.0f;
 #pragma unroll
-    for (int h = 0; h < GT; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+    for (int e = 0; e < 8; ++e) acc[e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     if (count <= 0) return;
 
-    auto full = [&](const Tile &t, int i) {
-      compute<false>(t, qb, tpos(i), pend, r16, g4, a.scale_log2, m_run, l_run, acc);
-    };
-    auto last_tile = [&](const Tile &t, int i) {
-      if (tpos(i) + kTile <= pend)
-        compute<false>(t, qb, tpos(i), pend, r16, g4, a.scale_log2, m_run, l_run, acc);
-      else
-        compute<true>(t, qb, tpos(i), pend, r16, g4, a.scale_log2, m_run, l_run, acc);
-    };
-
-    // Two tile buffers: while one is computed the other's loads are in
-    // flight, and the table entry after that is fetched one tile ahead.
-    // Every prefetch in the loop body is unconditional (the last one or two
-    // tiles are peeled), so the wait counts stay exact.
-    Tile A, B;
-    int64_t offA = lookup(0);
-    int64_t offB = lookup(1);
-    issue(A, kb, vb, offA, in_block(0), r16, g4);
-    int i = 0;
-    for (; i + 2 < count; i += 2) {
-      issue(B, kb, vb, offB, in_block(i + 1), r16, g4);
-      offA = lookup(i + 2);
-      full(A, i);
-      issue(A, kb, vb, offA, in_block(i + 2), r16, g4);
-      offB = lookup(i + 3);
-      full(B, i + 1);
-    }
-    if (i + 1 < count) {
-      issue(B, kb, vb, offB, in_block(i + 1), r16, g4);
-      last_tile(A, i);
-      last_tile(B, i + 1);
-    } else {
-      last_tile(A, i);
+    Tile ring[kDepth];
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) issue_tile(ring[k], k, entry(k));
+    int e_next = entry(kDepth);
+    for (int i0 = 0; i0 < count; i0 += kDepth) {
+#pragma unroll
+      for (int k = 0; k < kDepth; ++k) {
+        const int i = i0 + k;
+        if (i < count) {
+          if (tpos(i) + kTile <= pend)
+            compute<false>(ring[k], qb, tpos(i), pend, g4, a.scale_log2, m_run, l_run, acc);
+          else
+            compute<true>(ring[k], qb, tpos(i), pend, g4, a.scale_log2, m_run, l_run, acc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int e = e_next;
+        e_next = entry(i + kDepth + 1);
+        issue_tile(ring[k], i + kDepth, e);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 
@@ -408,6 +476,17 @@ struct Fast {
     *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + idx) = w;
   }
 
+  // this lane's 32 output dims (32*g4 .. +31 of head r16), scaled by mul:
+  // dims 32*g4 + 8*r + e sit in acc[e][r]
+  static __device__ __forceinline__ void store_lane(const DecodeArgs &a, int64_t idx,
+                                                    const f32x4_t (&acc)[8], float mul) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      store4(a, idx + 8 * r, make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]), mul);
+      store4(a, idx + 8 * r + 4, make_float4(acc[4][r], acc[5][r], acc[6][r], acc[7][r]), mul);
+    }
+  }
+
   static __device__ __forceinline__ float4 fma4(float4 x, float f, float4 acc) {
     return make_float4(fmaf(x.x, f, acc.x), fmaf(x.y, f, acc.y), fmaf(x.z, f, acc.z), fmaf(x.w, f, acc.w));
   }
@@ -425,19 +504,72 @@ struct Fast {
   // segment count merges the partials in wave order.
   // -------------------------------------------------------------------------
 
+  // Position in the batch's tile list: sequence s (n positions, nts tiles
+  // per unit, first global tile G), unit u (KV head * head groups + head
+  // group) and tile t of the unit.
+  struct Cursor {
+    int s, n, nts, u, t;
+    int64_t G;
+  };
+  static __device__ __forceinline__ int tiles_of(int n, int maxn) {
+    return (n > 0 && n <= maxn) ? (n + kTile - 1) / kTile : 0;
+  }
+  // next tile in list order (past the last one the cursor parks on s = S)
+  static __device__ __forceinline__ void advance(const DecodeArgs &a, Cursor &c, int KVG, int maxn) {
+    if (++c.t < c.nts) return;
+    c.t = 0;
+    if (++c.u < KVG) return;
+    c.u = 0;
+    c.G += static_cast<int64_t>(c.nts) * KVG;
+    for (;;) {
+      if (++c.s >= a.num_seqs) {
+        c.n = 0;
+        c.nts = 1;
+        return;
+      }
+      c.n = load_const(a.ctx, c.s);
+      c.nts = tiles_of(c.n, maxn);
+      if (c.nts > 0) return;
+    }
+  }
+
+  // q staging: 16-byte pieces, piece p = chunk p%16 of head p/16 of the unit
+  static constexpr int kQSlots = 8;
+  static constexpr int kQPieces = (GT * 16 + 63) / 64;
+  static __device__ __forceinline__ uint4 q_piece(const DecodeArgs &a, int s, int u, int p) {
+    const int kvh = u / a.head_groups;
+    const int hg = u - kvh * a.head_groups;
+    const int h = p >> 4;
+    if (p >= GT * 16 || h >= min(GT, a.group - hg * GT)) return make_uint4(0u, 0u, 0u, 0u);
+    const int64_t row = static_cast<int64_t>(s) * a.num_q_heads + kvh * a.group + hg * GT + h;
+    return *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + row * kHd + (p & 15) * 8);
+  }
+  // the staged q as the MFMA B operand (zero columns beyond the group)
+  static __device__ __forceinline__ void q_from_lds(const uint4 *slot, int hcount, int r16, int g4,
+                                                    V8 (&qb)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint4 w = make_uint4(0u, 0u, 0u, 0u);
+      if (r16 < hcount) w = slot[r16 * 16 + dbase(j, g4) / 8];
+      qb[j] = __builtin_bit_cast(V8, w);
+    }
+  }
+
   static __device__ __forceinline__ int64_t range_lo(int64_t T, int64_t W, int64_t w) {
     return T * w / W;
   }
-  // wave whose tile range holds global tile g
+  // wave whose tile range holds global tile g (T >= W >= 1, so no range is
+  // empty); g is clamped into [0, T) and the estimate into [0, W), so both
+  // correction loops end within W steps whatever they are given
   static __device__ __forceinline__ int64_t wave_of(int64_t T, int64_t W, int64_t g) {
-    int64_t w = g * W / T;
+    g = min(max(g, static_cast<int64_t>(0)), T - 1);
+    int64_t w = min(g * W / T, W - 1);
     while (w + 1 < W && range_lo(T, W, w + 1) <= g) ++w;
     while (w > 0 && range_lo(T, W, w) > g) --w;
     return w;
   }
 
   static __device__ void run_stream(const DecodeArgs &a) {
-    const int64_t W = gridDim.x;
     const int64_t w = blockIdx.x;
     const int lane = threadIdx.x;
     const int r16 = lane & 15;
@@ -449,8 +581,8 @@ struct Fast {
     auto tiles_of = [&](int n) { return (n > 0 && n <= maxn) ? (n + kTile - 1) / kTile : 0; };
 
     // rows of empty (zero) and out-of-range (NaN) sequences
-    for (int s = static_cast<int>(w); s < S; s += static_cast<int>(W)) {
-      const int n = a.ctx[s];
+    for (int s = static_cast<int>(w); s < S; s += static_cast<int>(gridDim.x)) {
+      const int n = load_const(a.ctx, s);
       if (n > 0 && n <= maxn) continue;
       const float fill = n == 0 ? 0.0f : nanv;
       for (int i = lane; i < a.num_q_heads * (kHd / 4); i += 64)
@@ -466,7 +598,12 @@ struct Fast {
       for (int o = 1; o < 64; o <<= 1) cnt += __shfl_xor(cnt, o, 64);
       T += cnt;
     }
-    T *= KVG;
+    T = uniform(T * KVG);
+    // the work is cut into min(grid, T) ranges, so every range holds at least
+    // one tile (an empty range would never count its partial in); the waves
+    // past that have nothing to do
+    const int64_t W = min(static_cast<int64_t>(gridDim.x), T);
+    if (w >= W) return;
     const int64_t lo = range_lo(T, W, w);
     const int64_t hi = range_lo(T, W, w + 1);
     if (lo >= hi) return;
@@ -482,139 +619,298 @@ struct Fast {
           const int64_t up = __shfl_up(incl, o, 64);
           if (lane >= o) incl += up;
         }
-        const int64_t total = __shfl(incl, 63, 64);
+        const int64_t total = uniform(__shfl(incl, 63, 64));
         if (base + total > lo) {
           const int first = __builtin_ctzll(__builtin_amdgcn_ballot_w64(base + incl > lo));
-          s = c0 + first;
-          G = base + __shfl(incl, first, 64) - __shfl(cnt, first, 64);
+          s = uniform(c0 + first);
+          G = uniform(base + __shfl(incl, first, 64) - __shfl(cnt, first, 64));
           break;
         }
         base += total;
       }
     }
-    int nts = tiles_of(a.ctx[s]);
-    int gidx = static_cast<int>((lo - G) / nts);
-    int t = static_cast<int>((lo - G) % nts);
+    Cursor c0;
+    c0.s = s;
+    c0.n = load_const(a.ctx, s);
+    c0.nts = tiles_of(c0.n);
+    c0.u = static_cast<int>((lo - G) / c0.nts);
+    c0.t = static_cast<int>((lo - G) % c0.nts);
+    c0.G = G;
 
-    for (int64_t g = lo; g < hi;) {
-      const int seg = static_cast<int>(min(hi - g, static_cast<int64_t>(nts - t)));
-      const int kvh = gidx / a.head_groups;
-      const int hg = gidx - kvh * a.head_groups;
-      const int hq0 = kvh * a.group + hg * GT;
-      const int hcount = min(GT, a.group - hg * GT);
-      const int64_t row0 = static_cast<int64_t>(s) * a.num_q_heads + hq0;
-      const int n = a.ctx[s];
-
-      V8 qb[4];
-      load_q(a, row0, hcount, r16, g4, qb);
-      const int64_t head_bytes = static_cast<int64_t>(BS) * kRow;
-      const uint8_t *kb = static_cast<const uint8_t *>(a.k_pool) + kvh * head_bytes;
-      const uint8_t *vb = static_cast<const uint8_t *>(a.v_pool) + kvh * head_bytes;
-      const int32_t *trow = a.tables + static_cast<int64_t>(s) * a.max_blocks;
-      bool bad = false;
-      float m_run, l_run, acc[GT][8];
-      accumulate(a, qb, kb, vb, trow, n, t, seg, 1, r16, g4, m_run, l_run, acc, bad);
-
-      l_run = xor32_sum(xor16_sum(l_run));
+    // q of the range's first kQSlots units, staged in LDS, so that starting
+    // a unit mid-stream never waits on a global load (that wait would also
+    // wait for every K/V load issued before it)
+    __shared__ uint4 s_q[kQSlots][GT * 16];
+    // the range's (at most two) partials, kept here until the stream is done
+    __shared__ f32x4_t s_po[2][GT * (kHd / 4)];
+    __shared__ f32x2_t s_pml[2][GT];
+    {
+      uint4 qv[kQSlots][kQPieces];
+      int nq = 0;
+      Cursor cu = c0;
+      int64_t gq = lo;
 #pragma unroll
-      for (int h = 0; h < GT; ++h)
+      for (int k = 0; k < kQSlots; ++k) {
+        if (gq < hi) {
+          nq = k + 1;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = xor32_sum(xor16_sum(acc[h][e]));
-      const bool any_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
-
-      if (t == 0 && seg == nts) {
-        // the whole unit is this wave's: write the output rows
-#pragma unroll
-        for (int h = 0; h < GT; ++h) {
-          const float lh = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_run), h));
-          if (h < hcount && g4 == (h & 3)) {
-            const float mul = any_bad ? nanv : a.v_scale / lh;
-            const int64_t base_idx = (row0 + h) * kHd + 8 * r16;
-            store4(a, base_idx, make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]), mul);
-            store4(a, base_idx + 4, make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]), mul);
-          }
+          for (int i = 0; i < kQPieces; ++i) qv[k][i] = q_piece(a, cu.s, cu.u, lane + 64 * i);
+          gq += cu.nts - cu.t;
+          cu.t = cu.nts - 1;
+          advance(a, cu, KVG, maxn);
         }
-      } else {
-        // a segment of a unit shared with neighbouring waves: publish a partial
-        const int slot = g == lo ? 0 : 1;
-        float *po = a.part_o + (w * 2 + slot) * (GT * kHd);
-        float *pml = a.part_m + (w * 2 + slot) * (GT * 2);
-        const float mul = any_bad ? nanv : 1.0f;
+      }
 #pragma unroll
-        for (int h = 0; h < GT; ++h) {
-          if (g4 == (h & 3)) {
-            float *dst = po + h * kHd + 8 * r16;
-            coherent_store4(dst, f32x4_t{acc[h][0] * mul, acc[h][1] * mul, acc[h][2] * mul, acc[h][3] * mul});
-            coherent_store4(dst + 4, f32x4_t{acc[h][4] * mul, acc[h][5] * mul, acc[h][6] * mul, acc[h][7] * mul});
-          }
-        }
-        if (g4 == 0 && r16 < GT) {
-          coherent_store(pml + 2 * r16, any_bad ? nanv : m_run);
-          coherent_store(pml + 2 * r16 + 1, any_bad ? nanv : l_run);
-        }
-        __builtin_amdgcn_s_waitcnt(0x0f70);      // vmcnt(0): the stores above have landed
-        const int64_t unit = static_cast<int64_t>(s) * KVG + gidx;
-        const int64_t gu = G + static_cast<int64_t>(gidx) * nts;          // unit's first tile
-        const int64_t wf = wave_of(T, W, gu);
-        const int64_t wl = wave_of(T, W, gu + nts - 1);
-        int last = 0;
-        if (lane == 0)
-          last = __hip_atomic_fetch_add(a.counters + unit, 1, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT) == static_cast<int>(wl - wf);
-        last = __builtin_amdgcn_readlane(last, 0);
-        if (last) {
-          // merge the unit's segments in wave order; row g4 merges heads
-          // g4, g4 + 4, ..., four segments' loads in flight at a time.
-          // A segment's partial sits in the first slot of its wave unless
-          // the wave's range began inside this unit's predecessor.
-          const int64_t wsplit = wave_of(T, W, gu) + (range_lo(T, W, wave_of(T, W, gu)) < gu ? 1 : 0);
-          for (int h = g4; h < hcount; h += 4) {
-            float big_m = -INFINITY, l = 0.0f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            bool nan_seen = false;
-            for (int64_t v0 = wf; v0 <= wl; v0 += 4) {
-              Partial x[4];
+      for (int k = 0; k < kQSlots; ++k)
+        if (k < nq)
 #pragma unroll
-              for (int k = 0; k < 4; ++k) {
-                const int64_t v = min(v0 + k, wl);
-                const int64_t sl = v < wsplit ? 1 : 0;
-                x[k].ml = coherent_load2(a.part_m + (v * 2 + sl) * (GT * 2) + 2 * h);
-                const float *src = a.part_o + (v * 2 + sl) * (GT * kHd) + h * kHd + 8 * r16;
-                x[k].o0 = coherent_load4(src);
-                x[k].o1 = coherent_load4(src + 4);
-              }
+          for (int i = 0; i < kQPieces; ++i)
+            if (lane + 64 * i < GT * 16) s_q[k][lane + 64 * i] = qv[k][i];
+    }
+    __syncthreads();
+
+    // One pipeline over the whole range: the issue cursor runs kDepth tiles
+    // ahead of the compute cursor and crosses unit boundaries freely, so
+    // the K/V stream never drains between units.
+    const int ko = k_lane_offset(r16, g4), vo = v_lane_offset(r16, g4);
+    const int64_t head_bytes = static_cast<int64_t>(BS) * kRow;
+    const int64_t blk_bytes = head_bytes * a.num_kv_heads;
+    const uint8_t *kpool = static_cast<const uint8_t *>(a.k_pool);
+    const uint8_t *vpool = static_cast<const uint8_t *>(a.v_pool);
+    auto entry_at = [&](const Cursor &c) {
+      return load_const(a.tables + static_cast<int64_t>(c.s) * a.max_blocks, c.t * kTile / BS);
+    };
+
+    Cursor ci = c0;                    // issue cursor
+    int64_t gi = lo;
+    int e_next = entry_at(ci);         // table entry of the tile at ci, fetched one issue ahead
+    uint32_t slot_bad = 0;             // bit k: ring slot k's table entry was out of range
+    auto issue_next = [&](Tile &tile, int k) {
+      int64_t off = 0;
+      bool on = false;
+      if (gi < hi) {
+        const int e = e_next;
+        const bool valid = static_cast<uint32_t>(e) < static_cast<uint32_t>(a.num_blocks);
+        slot_bad = valid ? (slot_bad & ~(1u << k)) : (slot_bad | (1u << k));
+        off = static_cast<int64_t>(valid ? e : 0) * blk_bytes + (ci.u / a.head_groups) * head_bytes +
+              (ci.t * kTile) % BS * kRow;
+        on = valid;
+        advance(a, ci, KVG, maxn);
+        if (gi + 1 < hi) e_next = entry_at(ci);
+      }
+      ++gi;
+      issue(tile, kpool, vpool, off, on, ko, vo);
+    };
+
+    Tile ring[kDepth];
 #pragma unroll
-              for (int k = 0; k < 4; ++k) {
-                coherent_wait(x[k].ml);
-                coherent_wait(x[k].o0);
-                coherent_wait(x[k].o1);
-              }
+    for (int k = 0; k < kDepth; ++k) issue_next(ring[k], k);
+
+    Cursor cc = c0;                    // compute cursor
+    int64_t gc = lo;
+    int nseg = 0;                      // segments started (q slot index)
+    int64_t seg_g0 = lo;
+    int seg_t0 = c0.t;
+    int hcount = 0;
+    int64_t row0 = 0;
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x4_t acc[8];
+    V8 qb[4];
+    bool bad = false;
+    // the range's split units (slot 0: its first unit, slot 1: its last),
+    // whose partials are counted in once the stream is done
+    Split sp0 = {}, sp1 = {};
+
+    for (int64_t g0 = lo; g0 < hi; g0 += kDepth) {
 #pragma unroll
-              for (int k = 0; k < 4; ++k)
-                if (v0 + k <= wl) fold(x[k], big_m, l, o, nan_seen);
+      for (int k = 0; k < kDepth; ++k) {
+        if (gc < hi) {
+          if (gc == lo || cc.t == 0) {
+            // a segment (the part of a unit inside the range) starts
+            seg_g0 = gc;
+            seg_t0 = cc.t;
+            const int kvh = cc.u / a.head_groups;
+            const int hg = cc.u - kvh * a.head_groups;
+            hcount = min(GT, a.group - hg * GT);
+            row0 = static_cast<int64_t>(cc.s) * a.num_q_heads + kvh * a.group + hg * GT;
+            if (nseg < kQSlots) {
+              q_from_lds(s_q[nseg], hcount, r16, g4, qb);
+            } else {
+              // past the staged units (very short contexts): a direct load,
+              // waited for here so no pending load leaks into the stream
+              load_q(a, row0, hcount, r16, g4, qb);
+              __builtin_amdgcn_s_waitcnt(0x0f70);    // vmcnt(0)
             }
-            const float mul2 = nan_seen ? nanv : a.v_scale / l;
-            const int64_t base_idx = (row0 + h) * kHd + 8 * r16;
-            store4(a, base_idx, make_float4(o[0], o[1], o[2], o[3]), mul2);
-            store4(a, base_idx + 4, make_float4(o[4], o[5], o[6], o[7]), mul2);
+            ++nseg;
+            m_run = -INFINITY;
+            l_run = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            bad = false;
           }
-          if (lane == 0)
-            __hip_atomic_store(a.counters + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
+          const int tp = cc.t * kTile;
+          if (tp + kTile <= cc.n)
+            compute<false>(ring[k], qb, tp, cc.n, g4, a.scale_log2, m_run, l_run, acc);
+          else
+            compute<true>(ring[k], qb, tp, cc.n, g4, a.scale_log2, m_run, l_run, acc);
+          bad |= ((slot_bad >> k) & 1u) != 0;
 
-      // next unit
-      g += seg;
-      t = 0;
-      if (++gidx == KVG) {
-        gidx = 0;
-        G += static_cast<int64_t>(nts) * KVG;
-        if (g < hi) {
-          do {
-            ++s;
-            nts = tiles_of(a.ctx[s]);
-          } while (nts == 0);
+          if (gc == hi - 1 || cc.t == cc.nts - 1) {
+            // the segment ends: the output rows if it is the whole unit, else
+            // this range's partial for the unit (published without waiting)
+            const float l = xor32_sum(xor16_sum(l_run));
+            if (seg_t0 == 0 && cc.t == cc.nts - 1) {
+              if (r16 < hcount)
+                store_lane(a, (row0 + r16) * kHd + 32 * g4, acc, bad ? nanv : a.v_scale / l);
+            } else {
+              // (written to global memory only after the stream: stores
+              // written through to the device-coherent level while the K/V
+              // loads stream slow the whole stream down)
+              const int slot = seg_g0 == lo ? 0 : 1;
+              const float mul = bad ? nanv : 1.0f;
+              if (r16 < GT) {
+                f32x4_t *dst = &s_po[slot][r16 * (kHd / 4) + 8 * g4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  dst[2 * r] = f32x4_t{acc[0][r], acc[1][r], acc[2][r], acc[3][r]} * mul;
+                  dst[2 * r + 1] = f32x4_t{acc[4][r], acc[5][r], acc[6][r], acc[7][r]} * mul;
+                }
+                if (g4 == 0) s_pml[slot][r16] = f32x2_t{bad ? nanv : m_run, bad ? nanv : l};
+              }
+              Split &sp = slot == 0 ? sp0 : sp1;
+              sp.on = true;
+              sp.unit = static_cast<int64_t>(cc.s) * KVG + cc.u;
+              sp.gu = cc.G + static_cast<int64_t>(cc.u) * cc.nts;
+              sp.nts = cc.nts;
+              sp.hcount = hcount;
+              sp.row0 = row0;
+            }
+          }
+          advance(a, cc, KVG, maxn);
+          ++gc;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        issue_next(ring[k], k);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // Publish the partials (device-coherent stores), wait until they have
+    // landed, count them in, and merge every unit whose last partial this was.
+    __syncthreads();
+    if (sp0.on) publish(a, w, 0, s_po[0], s_pml[0], lane);
+    if (sp1.on) publish(a, w, 1, s_po[1], s_pml[1], lane);
+    __builtin_amdgcn_s_waitcnt(0x0f70);      // vmcnt(0)
+    int last0 = 0, last1 = 0;
+    if (lane == 0) {
+      if (sp0.on)
+        last0 = __hip_atomic_fetch_add(a.counters + sp0.unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (sp1.on)
+        last1 = __hip_atomic_fetch_add(a.counters + sp1.unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    sp0.on = sp0.on && __builtin_amdgcn_readlane(last0, 0) == segments(T, W, sp0) - 1;
+    sp1.on = sp1.on && __builtin_amdgcn_readlane(last1, 0) == segments(T, W, sp1) - 1;
+    if (sp0.on || sp1.on) merge_units(a, T, W, sp0, sp1, r16, g4);
+  }
+
+  // write one of this range's partials from LDS to its global slot
+  static __device__ __forceinline__ void publish(const DecodeArgs &a, int64_t w, int slot, const f32x4_t *po,
+                                                 const f32x2_t *pml, int lane) {
+    float *go = a.part_o + (w * 2 + slot) * (GT * kHd);
+    float *gml = a.part_m + (w * 2 + slot) * (GT * 2);
+#pragma unroll
+    for (int i = lane; i < GT * (kHd / 4); i += 64) coherent_store4(go + 4 * i, po[i]);
+    if (lane < GT) {
+      coherent_store(gml + 2 * lane, pml[lane][0]);
+      coherent_store(gml + 2 * lane + 1, pml[lane][1]);
+    }
+  }
+
+  // One split unit of a range: its global index, first global tile, tile
+  // count, head count and first output row.
+  struct Split {
+    bool on;
+    int64_t unit, gu, row0;
+    int nts, hcount;
+  };
+
+  // number of ranges (partials) a split unit is cut into
+  static __device__ __forceinline__ int segments(int64_t T, int64_t W, const Split &sp) {
+    return static_cast<int>(wave_of(T, W, sp.gu + sp.nts - 1) - wave_of(T, W, sp.gu)) + 1;
+  }
+
+  // Merge the partials of up to two units (those with .on) in range order
+  // and write their output rows.  Row g4 of the wave merges heads g4, g4+4,
+  // ... of both units at once, four partials' loads in flight per unit.  A
+  // range's partial sits in its first slot unless the range began inside
+  // the unit's predecessor.  Leaves the units' counters at zero.
+  static __device__ void merge_units(const DecodeArgs &a, int64_t T, int64_t W, const Split &sp0,
+                                     const Split &sp1, int r16, int g4) {
+    const float nanv = __builtin_nanf("");
+    struct U {
+      bool on;
+      int64_t wf, wl, wsplit;
+    } u[2];
+    const Split *sp[2] = {&sp0, &sp1};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      u[k] = U{false, 0, 0, 0};
+      if (sp[k]->on) {
+        u[k].on = true;
+        u[k].wf = wave_of(T, W, sp[k]->gu);
+        u[k].wl = wave_of(T, W, sp[k]->gu + sp[k]->nts - 1);
+        u[k].wsplit = u[k].wf + (range_lo(T, W, u[k].wf) < sp[k]->gu ? 1 : 0);
+      }
+    }
+    const int hmax = max(sp0.on ? sp0.hcount : 0, sp1.on ? sp1.hcount : 0);
+    for (int h = g4; h < hmax; h += 4) {
+      float big_m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
+      float o[2][8] = {{0, 0, 0, 0, 0, 0, 0, 0}, {0, 0, 0, 0, 0, 0, 0, 0}};
+      bool nan_seen[2] = {false, false};
+      const int64_t span = max(u[0].on ? u[0].wl - u[0].wf : 0, u[1].on ? u[1].wl - u[1].wf : 0);
+      for (int64_t d0 = 0; d0 <= span; d0 += 4) {
+        Partial x[2][4];
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            // clamped to a valid partial; only the live ones are folded
+            const int64_t v = u[k].on ? min(u[k].wf + d0 + j, u[k].wl) : 0;
+            const int64_t sl = u[k].on && v < u[k].wsplit ? 1 : 0;
+            const int hh = min(h, GT - 1);
+            x[k][j].ml = coherent_load2(a.part_m + (v * 2 + sl) * (GT * 2) + 2 * hh);
+            const float *src = a.part_o + (v * 2 + sl) * (GT * kHd) + hh * kHd + 8 * r16;
+            x[k][j].o0 = coherent_load4(src);
+            x[k][j].o1 = coherent_load4(src + 4);
+          }
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            coherent_wait(x[k][j].ml);
+            coherent_wait(x[k][j].o0);
+            coherent_wait(x[k][j].o1);
+          }
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (u[k].on && h < sp[k]->hcount && u[k].wf + d0 + j <= u[k].wl)
+              fold(x[k][j], big_m[k], l[k], o[k], nan_seen[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        if (u[k].on && h < sp[k]->hcount) {
+          const float mul = nan_seen[k] ? nanv : a.v_scale / l[k];
+          const int64_t base_idx = (sp[k]->row0 + h) * kHd + 8 * r16;
+          store4(a, base_idx, make_float4(o[k][0], o[k][1], o[k][2], o[k][3]), mul);
+          store4(a, base_idx + 4, make_float4(o[k][4], o[k][5], o[k][6], o[k][7]), mul);
         }
       }
+    }
+    if (threadIdx.x == 0) {
+      if (sp0.on) __hip_atomic_store(a.counters + sp0.unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (sp1.on) __hip_atomic_store(a.counters + sp1.unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
@@ -632,7 +928,7 @@ struct Fast {
     const int lane = tid & 63;
     const int r16 = lane & 15;
     const int g4 = lane >> 4;
-    const int n = a.ctx[seq];
+    const int n = load_const(a.ctx, seq);
     const int hq0 = kvh * a.group + hg * GT;
     const int hcount = min(GT, a.group - hg * GT);
     const int64_t row0 = static_cast<int64_t>(seq) * a.num_q_heads + hq0;
@@ -661,21 +957,19 @@ struct Fast {
     const uint8_t *vb = static_cast<const uint8_t *>(a.v_pool) + kvh * head_bytes;
     const int32_t *trow = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
     bool bad = false;
-    float m_run, l_run, acc[GT][8];
+    float m_run, l_run;
+    f32x4_t acc[8];
     accumulate(a, qb, kb, vb, trow, pend, pstart / kTile + wave, nloc, NW, r16, g4, m_run, l_run, acc,
                bad);
 
-    // add the four row groups' partial sums, then hand the wave's state to LDS
+    // add the four row groups' sums of exponentials, then hand the wave's
+    // state to LDS (lane (h, g4) holds dims 32*g4 .. +31 of head h)
     l_run = xor32_sum(xor16_sum(l_run));
+    if (r16 < GT) {
 #pragma unroll
-    for (int h = 0; h < GT; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = xor32_sum(xor16_sum(acc[h][e]));
-#pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      if (g4 == (h & 3)) {
-        s_acc[wave][h][2 * r16] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-        s_acc[wave][h][2 * r16 + 1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+      for (int r = 0; r < 4; ++r) {
+        s_acc[wave][r16][8 * g4 + 2 * r] = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+        s_acc[wave][r16][8 * g4 + 2 * r + 1] = make_float4(acc[4][r], acc[5][r], acc[6][r], acc[7][r]);
       }
     }
     if (g4 == 0 && r16 < GT) {
@@ -781,9 +1075,9 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs a) {
   Fast<QS, KS, GT, BS, 1>::run_stream(a);
 }
 
-// Grid of the balanced split: as many single-wave workgroups as the GPU
-// keeps resident (occupancy of this kernel x compute units), capped by the
-// workspace capacity the caller sized for.
+// Grid of the balanced split: one single-wave workgroup per SIMD (fewer if
+// this kernel's occupancy is lower), capped by the workspace capacity the
+// caller sized for.
 template <typename QS, typename KS, int GT, int BS>
 hipError_t launch_stream_gt(const DecodeArgs &a, hipStream_t s) {
   static const int per_cu = [] {
@@ -793,7 +1087,7 @@ hipError_t launch_stream_gt(const DecodeArgs &a, hipStream_t s) {
       n = 8;
     return n;
   }();
-  const int waves = min(a.stream_waves, device_compute_units() * per_cu);
+  const int waves = min(a.stream_waves, device_compute_units() * min(per_cu, kMaxStreamWavesPerCu));
   hipLaunchKernelGGL((decode_stream_kernel<QS, KS, GT, BS>), dim3(waves), dim3(64), 0, s, a);
   return hipGetLastError();
 }

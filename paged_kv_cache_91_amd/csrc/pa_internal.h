@@ -86,9 +86,11 @@ inline int device_compute_units() {
   return cus;
 }
 
-// Upper bound on resident single-wave workgroups per compute unit that the
-// balanced split may launch (its workspace is sized for this many).
-constexpr int kMaxStreamWavesPerCu = 16;
+// Single-wave workgroups per compute unit that the balanced split launches
+// (its workspace is sized for this many): one per SIMD.  A second wave on a
+// SIMD only gets the issue slots the first leaves over, falls behind it and
+// finishes its share late, with too few loads in flight to keep HBM busy.
+constexpr int kMaxStreamWavesPerCu = 4;
 
 // Workspace layout shared by the API layer and the kernels.
 struct WorkspaceLayout {

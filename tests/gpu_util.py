@@ -109,6 +109,10 @@ class DeviceWorkload:
         pa.pa_copy_blocks(self.pool, pairs)
 
     def decode(self, partition_size: int = 0, out: torch.Tensor = None) -> torch.Tensor:
+        if out is None:
+            # NaN-filled, so a row the kernels never write cannot pass with
+            # values a previous call left in recycled memory
+            out = torch.full_like(self.q, float("nan"))
         return pa.pa_decode(self.q, self.pool, self.tables, self.ctx, self.wl.scale, out=out,
                             partition_size=partition_size, q_dtype=self.wl.q_dtype)
 

@@ -82,7 +82,8 @@ def test_scalar_case_exactly_three():
         tables = torch.tensor([placement], dtype=torch.int32, device=DEV)
         ctx = torch.tensor([5], dtype=torch.int32, device=DEV)
         for part in (0, 4):
-            out = pa.pa_decode(q, pool, tables, ctx, 1.0, partition_size=part)
+            out = pa.pa_decode(q, pool, tables, ctx, 1.0, out=torch.full_like(q, float("nan")),
+                               partition_size=part)
             assert out.cpu().numpy().tolist() == [[[3.0] * d]], (placement, part)
 
 
@@ -292,6 +293,23 @@ def test_edge_lengths():
     outs = check_decode(wl, parts=(0, 16, 32, pa.PA_PARTITION_AUTO))
     for o in outs:
         assert not o[0].any() and not o[5].any()          # n == 0: zero rows
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_many_short_contexts(kv):
+    """Over a thousand 1-2 tile contexts: in the balanced split a wave's tile
+    range then spans about ten (sequence, head group) units, past the ones
+    whose q is staged ahead, with whole units and split ones mixed."""
+    rng = np.random.default_rng(51)
+    lens = rng.integers(1, 25, size=1200)
+    need = sum(-(-int(n) // 16) for n in lens)
+    common = dict(q_dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                  num_blocks=need + 3, context_lens=lens, rng=rng)
+    if kv == "bf16":
+        wl = W.build_decode(51, name="short", kv_dtype="bf16", **common)
+    else:
+        wl = W.build_write_filled(51, name="short-fp8", src_dtype="bf16", kv_dtype="fp8_e4m3", **common)
+    check_decode(wl, parts=(0, pa.PA_PARTITION_AUTO))
 
 
 def test_out_of_range_table_entry_and_length_give_nan_rows():
