@@ -555,44 +555,51 @@ struct Fast {
     }
   }
 
+  // floor(a / b) for 0 <= a < 2^53 and 0 < b < 2^31: the double quotient is
+  // within one of the exact one, and one integer check on each side fixes
+  // it (a 64-bit integer division is a long instruction sequence here)
+  static __device__ __forceinline__ int64_t floor_div(int64_t a, int64_t b) {
+    int64_t q = static_cast<int64_t>(static_cast<double>(a) / static_cast<double>(b));
+    if (q * b > a)
+      --q;
+    else if ((q + 1) * b <= a)
+      ++q;
+    return q;
+  }
+  // first tile of range w (T * W < 2^53, i.e. fewer than 2^40 tiles)
   static __device__ __forceinline__ int64_t range_lo(int64_t T, int64_t W, int64_t w) {
-    return T * w / W;
+    return floor_div(T * w, W);
   }
   // wave whose tile range holds global tile g (T >= W >= 1, so no range is
-  // empty); g is clamped into [0, T) and the estimate into [0, W), so both
-  // correction loops end within W steps whatever they are given
+  // empty): the last w with floor(T w / W) <= g, i.e. floor(((g+1) W - 1) / T);
+  // g is clamped into [0, T) first
   static __device__ __forceinline__ int64_t wave_of(int64_t T, int64_t W, int64_t g) {
     g = min(max(g, static_cast<int64_t>(0)), T - 1);
-    int64_t w = min(g * W / T, W - 1);
-    while (w + 1 < W && range_lo(T, W, w + 1) <= g) ++w;
-    while (w > 0 && range_lo(T, W, w) > g) --w;
-    return w;
+    return min(floor_div((g + 1) * W - 1, T), W - 1);
   }
 
   static __device__ void run_stream(const DecodeArgs &a) {
     const int64_t w = blockIdx.x;
     const int lane = threadIdx.x;
-    const int r16 = lane & 15;
-    const int g4 = lane >> 4;
     const int S = a.num_seqs;
     const int KVG = a.num_kv_heads * a.head_groups;
     const int maxn = a.max_blocks * BS;
     const float nanv = __builtin_nanf("");
     auto tiles_of = [&](int n) { return (n > 0 && n <= maxn) ? (n + kTile - 1) / kTile : 0; };
 
-    // rows of empty (zero) and out-of-range (NaN) sequences
-    for (int s = static_cast<int>(w); s < S; s += static_cast<int>(gridDim.x)) {
-      const int n = load_const(a.ctx, s);
-      if (n > 0 && n <= maxn) continue;
-      const float fill = n == 0 ? 0.0f : nanv;
-      for (int i = lane; i < a.num_q_heads * (kHd / 4); i += 64)
-        store4(a, (static_cast<int64_t>(s) * a.num_q_heads + (i >> 5)) * kHd + 4 * (i & 31),
-               make_float4(fill, fill, fill, fill), 1.0f);
+    // total tiles, then the sequence holding this wave's first tile; the
+    // first 64 lengths stay in registers, so for up to 64 sequences one load
+    // serves both steps
+    const int n_lane = lane < S ? a.ctx[lane] : 0;
+    const int64_t cnt0 = tiles_of(n_lane);
+    int64_t incl0 = cnt0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t up = __shfl_up(incl0, o, 64);
+      if (lane >= o) incl0 += up;
     }
-
-    // total tiles, then the sequence holding this wave's first tile
-    int64_t T = 0;
-    for (int c0 = 0; c0 < S; c0 += 64) {
+    int64_t T = uniform(__shfl(incl0, 63, 64));
+    for (int c0 = 64; c0 < S; c0 += 64) {
       int64_t cnt = (c0 + lane < S) ? tiles_of(a.ctx[c0 + lane]) : 0;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) cnt += __shfl_xor(cnt, o, 64);
@@ -603,38 +610,72 @@ struct Fast {
     // one tile (an empty range would never count its partial in); the waves
     // past that have nothing to do
     const int64_t W = min(static_cast<int64_t>(gridDim.x), T);
-    if (w >= W) return;
-    const int64_t lo = range_lo(T, W, w);
-    const int64_t hi = range_lo(T, W, w + 1);
-    if (lo >= hi) return;
-    int s = 0;
+    const int64_t lo = w < W ? range_lo(T, W, w) : 0;
+    const int64_t hi = w < W ? range_lo(T, W, w + 1) : 0;
+    if (lo < hi) stream(a, T, W, w, lo, hi, n_lane, cnt0, incl0);
+
+    // rows of empty (zero) and out-of-range (NaN) sequences
+    for (int s = static_cast<int>(w); s < S; s += static_cast<int>(gridDim.x)) {
+      const int n = load_const(a.ctx, s);
+      if (n > 0 && n <= maxn) continue;
+      const float fill = n == 0 ? 0.0f : nanv;
+      for (int i = lane; i < a.num_q_heads * (kHd / 4); i += 64)
+        store4(a, (static_cast<int64_t>(s) * a.num_q_heads + (i >> 5)) * kHd + 4 * (i & 31),
+               make_float4(fill, fill, fill, fill), 1.0f);
+    }
+  }
+
+  // The wave's tile range [lo, hi) of the T-tile list cut into W ranges.
+  // n_lane / cnt0 / incl0: the first 64 sequences' lengths, tile counts and
+  // their inclusive running sum, one per lane.
+  static __device__ void stream(const DecodeArgs &a, int64_t T, int64_t W, int64_t w, int64_t lo,
+                                int64_t hi, int n_lane, int64_t cnt0, int64_t incl0) {
+    const int lane = threadIdx.x;
+    const int r16 = lane & 15;
+    const int g4 = lane >> 4;
+    const int S = a.num_seqs;
+    const int KVG = a.num_kv_heads * a.head_groups;
+    const int maxn = a.max_blocks * BS;
+    const float nanv = __builtin_nanf("");
+    auto tiles_of = [&](int n) { return (n > 0 && n <= maxn) ? (n + kTile - 1) / kTile : 0; };
+
+    int s = 0, n0 = 0;
     int64_t G = 0;                     // first global tile of sequence s
     {
-      int64_t base = 0;
-      for (int c0 = 0; c0 < S; c0 += 64) {
-        const int64_t cnt = ((c0 + lane < S) ? tiles_of(a.ctx[c0 + lane]) : 0) * static_cast<int64_t>(KVG);
-        int64_t incl = cnt;
+      const int64_t total0 = uniform(__shfl(incl0, 63, 64)) * KVG;
+      if (total0 > lo) {
+        const int first = __builtin_ctzll(__builtin_amdgcn_ballot_w64(incl0 * KVG > lo));
+        s = uniform(first);
+        G = uniform((__shfl(incl0, first, 64) - __shfl(cnt0, first, 64)) * KVG);
+        n0 = __builtin_amdgcn_readlane(n_lane, first);
+      } else {
+        int64_t base = total0;
+        for (int c0 = 64; c0 < S; c0 += 64) {
+          const int64_t cnt = ((c0 + lane < S) ? tiles_of(a.ctx[c0 + lane]) : 0) * static_cast<int64_t>(KVG);
+          int64_t incl = cnt;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int64_t up = __shfl_up(incl, o, 64);
-          if (lane >= o) incl += up;
+          for (int o = 1; o < 64; o <<= 1) {
+            const int64_t up = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += up;
+          }
+          const int64_t total = uniform(__shfl(incl, 63, 64));
+          if (base + total > lo) {
+            const int first = __builtin_ctzll(__builtin_amdgcn_ballot_w64(base + incl > lo));
+            s = uniform(c0 + first);
+            G = uniform(base + __shfl(incl, first, 64) - __shfl(cnt, first, 64));
+            n0 = load_const(a.ctx, s);
+            break;
+          }
+          base += total;
         }
-        const int64_t total = uniform(__shfl(incl, 63, 64));
-        if (base + total > lo) {
-          const int first = __builtin_ctzll(__builtin_amdgcn_ballot_w64(base + incl > lo));
-          s = uniform(c0 + first);
-          G = uniform(base + __shfl(incl, first, 64) - __shfl(cnt, first, 64));
-          break;
-        }
-        base += total;
       }
     }
     Cursor c0;
     c0.s = s;
-    c0.n = load_const(a.ctx, s);
+    c0.n = n0;
     c0.nts = tiles_of(c0.n);
-    c0.u = static_cast<int>((lo - G) / c0.nts);
-    c0.t = static_cast<int>((lo - G) % c0.nts);
+    c0.u = static_cast<int>(floor_div(lo - G, c0.nts));
+    c0.t = static_cast<int>(lo - G - static_cast<int64_t>(c0.u) * c0.nts);
     c0.G = G;
 
     // q of the range's first kQSlots units, staged in LDS, so that starting
@@ -808,8 +849,17 @@ struct Fast {
       if (sp1.on)
         last1 = __hip_atomic_fetch_add(a.counters + sp1.unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    sp0.on = sp0.on && __builtin_amdgcn_readlane(last0, 0) == segments(T, W, sp0) - 1;
-    sp1.on = sp1.on && __builtin_amdgcn_readlane(last1, 0) == segments(T, W, sp1) - 1;
+    // the unit's first and last range (worked out while the atomics fly)
+    if (sp0.on) {
+      sp0.wf = wave_of(T, W, sp0.gu);
+      sp0.wl = wave_of(T, W, sp0.gu + sp0.nts - 1);
+    }
+    if (sp1.on) {
+      sp1.wf = wave_of(T, W, sp1.gu);
+      sp1.wl = wave_of(T, W, sp1.gu + sp1.nts - 1);
+    }
+    sp0.on = sp0.on && __builtin_amdgcn_readlane(last0, 0) == static_cast<int>(sp0.wl - sp0.wf);
+    sp1.on = sp1.on && __builtin_amdgcn_readlane(last1, 0) == static_cast<int>(sp1.wl - sp1.wf);
     if (sp0.on || sp1.on) merge_units(a, T, W, sp0, sp1, r16, g4);
   }
 
@@ -827,17 +877,13 @@ struct Fast {
   }
 
   // One split unit of a range: its global index, first global tile, tile
-  // count, head count and first output row.
+  // count, head count, first output row, and the first and last range that
+  // hold part of it (wl - wf + 1 partials).
   struct Split {
     bool on;
-    int64_t unit, gu, row0;
+    int64_t unit, gu, row0, wf, wl;
     int nts, hcount;
   };
-
-  // number of ranges (partials) a split unit is cut into
-  static __device__ __forceinline__ int segments(int64_t T, int64_t W, const Split &sp) {
-    return static_cast<int>(wave_of(T, W, sp.gu + sp.nts - 1) - wave_of(T, W, sp.gu)) + 1;
-  }
 
   // Merge the partials of up to two units (those with .on) in range order
   // and write their output rows.  Row g4 of the wave merges heads g4, g4+4,
@@ -857,8 +903,8 @@ struct Fast {
       u[k] = U{false, 0, 0, 0};
       if (sp[k]->on) {
         u[k].on = true;
-        u[k].wf = wave_of(T, W, sp[k]->gu);
-        u[k].wl = wave_of(T, W, sp[k]->gu + sp[k]->nts - 1);
+        u[k].wf = sp[k]->wf;
+        u[k].wl = sp[k]->wl;
         u[k].wsplit = u[k].wf + (range_lo(T, W, u[k].wf) < sp[k]->gu ? 1 : 0);
       }
     }
