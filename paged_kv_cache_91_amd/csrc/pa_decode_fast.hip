@@ -514,8 +514,10 @@ struct Fast {
   static __device__ __forceinline__ int tiles_of(int n, int maxn) {
     return (n > 0 && n <= maxn) ? (n + kTile - 1) / kTile : 0;
   }
-  // next tile in list order (past the last one the cursor parks on s = S)
-  static __device__ __forceinline__ void advance(const DecodeArgs &a, Cursor &c, int KVG, int maxn) {
+  // next tile in list order (past the last one the cursor parks on s = S);
+  // n_lane holds the first 64 sequences' lengths, one per lane
+  static __device__ __forceinline__ void advance(const DecodeArgs &a, Cursor &c, int KVG, int maxn,
+                                                 int n_lane) {
     if (++c.t < c.nts) return;
     c.t = 0;
     if (++c.u < KVG) return;
@@ -527,7 +529,7 @@ struct Fast {
         c.nts = 1;
         return;
       }
-      c.n = load_const(a.ctx, c.s);
+      c.n = c.s < 64 ? __builtin_amdgcn_readlane(n_lane, c.s) : load_const(a.ctx, c.s);
       c.nts = tiles_of(c.n, maxn);
       if (c.nts > 0) return;
     }
@@ -678,6 +680,22 @@ struct Fast {
     c0.t = static_cast<int>(lo - G - static_cast<int64_t>(c0.u) * c0.nts);
     c0.G = G;
 
+    // Set-up order: the first table entry, the q loads, then the first
+    // kDepth tiles' loads, and only then the q stores to LDS (whose wait for
+    // the q loads leaves the tile loads in flight).
+    const int ko = k_lane_offset(r16, g4), vo = v_lane_offset(r16, g4);
+    const int64_t head_bytes = static_cast<int64_t>(BS) * kRow;
+    const int64_t blk_bytes = head_bytes * a.num_kv_heads;
+    const uint8_t *kpool = static_cast<const uint8_t *>(a.k_pool);
+    const uint8_t *vpool = static_cast<const uint8_t *>(a.v_pool);
+    auto entry_at = [&](const Cursor &c) {
+      return load_const(a.tables + static_cast<int64_t>(c.s) * a.max_blocks, c.t * kTile / BS);
+    };
+    Cursor ci = c0;                    // issue cursor
+    int64_t gi = lo;
+    int e_next = entry_at(ci);         // table entry of the tile at ci, fetched one issue ahead
+    uint32_t slot_bad = 0;             // bit k: ring slot k's table entry was out of range
+
     // q of the range's first kQSlots units, staged in LDS, so that starting
     // a unit mid-stream never waits on a global load (that wait would also
     // wait for every K/V load issued before it)
@@ -685,9 +703,9 @@ struct Fast {
     // the range's (at most two) partials, kept here until the stream is done
     __shared__ f32x4_t s_po[2][GT * (kHd / 4)];
     __shared__ f32x2_t s_pml[2][GT];
+    uint4 qv[kQSlots][kQPieces];
+    int nq = 0;
     {
-      uint4 qv[kQSlots][kQPieces];
-      int nq = 0;
       Cursor cu = c0;
       int64_t gq = lo;
 #pragma unroll
@@ -698,34 +716,14 @@ struct Fast {
           for (int i = 0; i < kQPieces; ++i) qv[k][i] = q_piece(a, cu.s, cu.u, lane + 64 * i);
           gq += cu.nts - cu.t;
           cu.t = cu.nts - 1;
-          advance(a, cu, KVG, maxn);
+          advance(a, cu, KVG, maxn, n_lane);
         }
       }
-#pragma unroll
-      for (int k = 0; k < kQSlots; ++k)
-        if (k < nq)
-#pragma unroll
-          for (int i = 0; i < kQPieces; ++i)
-            if (lane + 64 * i < GT * 16) s_q[k][lane + 64 * i] = qv[k][i];
     }
-    __syncthreads();
 
     // One pipeline over the whole range: the issue cursor runs kDepth tiles
     // ahead of the compute cursor and crosses unit boundaries freely, so
     // the K/V stream never drains between units.
-    const int ko = k_lane_offset(r16, g4), vo = v_lane_offset(r16, g4);
-    const int64_t head_bytes = static_cast<int64_t>(BS) * kRow;
-    const int64_t blk_bytes = head_bytes * a.num_kv_heads;
-    const uint8_t *kpool = static_cast<const uint8_t *>(a.k_pool);
-    const uint8_t *vpool = static_cast<const uint8_t *>(a.v_pool);
-    auto entry_at = [&](const Cursor &c) {
-      return load_const(a.tables + static_cast<int64_t>(c.s) * a.max_blocks, c.t * kTile / BS);
-    };
-
-    Cursor ci = c0;                    // issue cursor
-    int64_t gi = lo;
-    int e_next = entry_at(ci);         // table entry of the tile at ci, fetched one issue ahead
-    uint32_t slot_bad = 0;             // bit k: ring slot k's table entry was out of range
     auto issue_next = [&](Tile &tile, int k) {
       int64_t off = 0;
       bool on = false;
@@ -736,7 +734,7 @@ struct Fast {
         off = static_cast<int64_t>(valid ? e : 0) * blk_bytes + (ci.u / a.head_groups) * head_bytes +
               (ci.t * kTile) % BS * kRow;
         on = valid;
-        advance(a, ci, KVG, maxn);
+        advance(a, ci, KVG, maxn, n_lane);
         if (gi + 1 < hi) e_next = entry_at(ci);
       }
       ++gi;
@@ -746,6 +744,14 @@ struct Fast {
     Tile ring[kDepth];
 #pragma unroll
     for (int k = 0; k < kDepth; ++k) issue_next(ring[k], k);
+
+#pragma unroll
+    for (int k = 0; k < kQSlots; ++k)
+      if (k < nq)
+#pragma unroll
+        for (int i = 0; i < kQPieces; ++i)
+          if (lane + 64 * i < GT * 16) s_q[k][lane + 64 * i] = qv[k][i];
+    __syncthreads();
 
     Cursor cc = c0;                    // compute cursor
     int64_t gc = lo;
@@ -827,7 +833,7 @@ struct Fast {
               sp.row0 = row0;
             }
           }
-          advance(a, cc, KVG, maxn);
+          advance(a, cc, KVG, maxn, n_lane);
           ++gc;
         }
         __builtin_amdgcn_sched_barrier(0);
