@@ -376,56 +376,62 @@ hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s, bool *supported) 
 // cache write
 // ---------------------------------------------------------------------------
 
+// Thread i of a write handles piece i % 2^units_log2 of row i >> units_log2,
+// row r = token * num_kv_heads + head.  The source bytes do not depend on
+// the slot, so they are loaded before it: one memory round trip, not two.
+// (r / heads is done in 32 bits whenever r fits, as in every realistic batch.)
+__device__ __forceinline__ int64_t write_token(int64_t r, int heads) {
+  return r < (int64_t{1} << 32) ? static_cast<int64_t>(static_cast<uint32_t>(r) / static_cast<uint32_t>(heads))
+                                : r / heads;
+}
+
 // Same-dtype write: one thread moves UNIT bytes of one (token, head) row.
 template <int UNIT>
-__global__ __launch_bounds__(256) void write_copy_kernel(WriteArgs a, int row_bytes) {
+__global__ __launch_bounds__(256) void write_copy_kernel(WriteArgs a, int units_log2) {
   using U = typename std::conditional<UNIT == 16, uint4, uint2>::type;
-  const int units = row_bytes / UNIT;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t total = static_cast<int64_t>(a.num_tokens) * a.num_kv_heads * units;
-  if (i >= total) return;
-  const int u = static_cast<int>(i % units);
-  const int64_t th = i / units;
-  const int h = static_cast<int>(th % a.num_kv_heads);
-  const int64_t t = th / a.num_kv_heads;
+  const int64_t r = i >> units_log2;
+  if (r >= static_cast<int64_t>(a.num_tokens) * a.num_kv_heads) return;
+  const int64_t row_bytes = static_cast<int64_t>(UNIT) << units_log2;
+  const int64_t piece = (i & ((int64_t{1} << units_log2) - 1)) * UNIT;
+  const int64_t src = r * row_bytes + piece;
+  const U kx = *reinterpret_cast<const U *>(static_cast<const uint8_t *>(a.k) + src);
+  const U vx = *reinterpret_cast<const U *>(static_cast<const uint8_t *>(a.v) + src);
+  const int64_t t = write_token(r, a.num_kv_heads);
+  const int64_t h = r - t * a.num_kv_heads;
   const int64_t slot = a.slots[t];
   if (slot < 0 || slot >= a.num_slots) return;
   const int64_t blk = slot >> a.bs_log2;
   const int64_t off = slot & ((1 << a.bs_log2) - 1);
-  const int64_t dst = (((blk * a.num_kv_heads + h) << a.bs_log2) + off) * row_bytes + static_cast<int64_t>(u) * UNIT;
-  const int64_t src = th * row_bytes + static_cast<int64_t>(u) * UNIT;
-  *reinterpret_cast<U *>(static_cast<uint8_t *>(a.k_pool) + dst) =
-      *reinterpret_cast<const U *>(static_cast<const uint8_t *>(a.k) + src);
-  *reinterpret_cast<U *>(static_cast<uint8_t *>(a.v_pool) + dst) =
-      *reinterpret_cast<const U *>(static_cast<const uint8_t *>(a.v) + src);
+  const int64_t dst = (((blk * a.num_kv_heads + h) << a.bs_log2) + off) * row_bytes + piece;
+  *reinterpret_cast<U *>(static_cast<uint8_t *>(a.k_pool) + dst) = kx;
+  *reinterpret_cast<U *>(static_cast<uint8_t *>(a.v_pool) + dst) = vx;
 }
 
 // Quantising write into an e4m3 pool: one thread encodes 8 elements
 // (4 for float sources: one 16-byte source load either way).
 template <typename SS>
-__global__ __launch_bounds__(256) void write_fp8_kernel(WriteArgs a) {
+__global__ __launch_bounds__(256) void write_fp8_kernel(WriteArgs a, int units_log2) {
   constexpr int E = std::is_same<SS, F32S>::value ? 4 : 8;
-  const int units = a.head_dim / E;
+  using KV = Kv<SS>;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t total = static_cast<int64_t>(a.num_tokens) * a.num_kv_heads * units;
-  if (i >= total) return;
-  const int u = static_cast<int>(i % units);
-  const int64_t th = i / units;
-  const int h = static_cast<int>(th % a.num_kv_heads);
-  const int64_t t = th / a.num_kv_heads;
+  const int64_t r = i >> units_log2;
+  if (r >= static_cast<int64_t>(a.num_tokens) * a.num_kv_heads) return;
+  const int64_t elem = (i & ((int64_t{1} << units_log2) - 1)) * E;
+  const int64_t src = (r * a.head_dim + elem) * KV::kSize;
+  const uint4 raw[2] = {*reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(a.k) + src),
+                        *reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(a.v) + src)};
+  const int64_t t = write_token(r, a.num_kv_heads);
+  const int64_t h = r - t * a.num_kv_heads;
   const int64_t slot = a.slots[t];
   if (slot < 0 || slot >= a.num_slots) return;
   const int64_t blk = slot >> a.bs_log2;
   const int64_t off = slot & ((1 << a.bs_log2) - 1);
-  const int64_t dst = (((blk * a.num_kv_heads + h) << a.bs_log2) + off) * a.head_dim + static_cast<int64_t>(u) * E;
-  const int64_t src = th * a.head_dim + static_cast<int64_t>(u) * E;
-  using KV = Kv<SS>;
+  const int64_t dst = (((blk * a.num_kv_heads + h) << a.bs_log2) + off) * a.head_dim + elem;
   for (int which = 0; which < 2; ++which) {
-    const uint8_t *sp = static_cast<const uint8_t *>(which ? a.v : a.k) + src * KV::kSize;
     const float inv = which ? a.v_inv : a.k_inv;
-    const uint4 raw = *reinterpret_cast<const uint4 *>(sp);
     float f[8];
-    KV::widen(raw, f);
+    KV::widen(raw[which], f);
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < E; ++e) w[e >> 2] |= f32_to_e4m3(f[e] * inv) << (8 * (e & 3));
@@ -473,6 +479,13 @@ hipError_t launch_decode(int q_dtype, int kv_dtype, const DecodeArgs &a, hipStre
   return hipSuccess;
 }
 
+// log2 of a power of two
+static int log2_int(int x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+
 hipError_t launch_write(int src_dtype, int dst_dtype, const WriteArgs &a, hipStream_t s,
                         bool *supported) {
   if (supported) *supported = true;
@@ -481,12 +494,13 @@ hipError_t launch_write(int src_dtype, int dst_dtype, const WriteArgs &a, hipStr
     const int esize = src_dtype == kF32 ? 4 : (src_dtype == kFP8 ? 1 : 2);
     const int row_bytes = a.head_dim * esize;
     const int unit = (row_bytes % 16 == 0) ? 16 : 8;
+    const int units_log2 = log2_int(row_bytes / unit);
     const int64_t total = static_cast<int64_t>(a.num_tokens) * a.num_kv_heads * (row_bytes / unit);
     const dim3 grid(static_cast<unsigned>((total + threads - 1) / threads));
     if (unit == 16)
-      hipLaunchKernelGGL((write_copy_kernel<16>), grid, dim3(threads), 0, s, a, row_bytes);
+      hipLaunchKernelGGL((write_copy_kernel<16>), grid, dim3(threads), 0, s, a, units_log2);
     else
-      hipLaunchKernelGGL((write_copy_kernel<8>), grid, dim3(threads), 0, s, a, row_bytes);
+      hipLaunchKernelGGL((write_copy_kernel<8>), grid, dim3(threads), 0, s, a, units_log2);
     return hipGetLastError();
   }
   if (dst_dtype != kFP8) {
@@ -494,12 +508,13 @@ hipError_t launch_write(int src_dtype, int dst_dtype, const WriteArgs &a, hipStr
     return hipSuccess;
   }
   const int e = src_dtype == kF32 ? 4 : 8;
+  const int units_log2 = log2_int(a.head_dim / e);
   const int64_t total = static_cast<int64_t>(a.num_tokens) * a.num_kv_heads * (a.head_dim / e);
   const dim3 grid(static_cast<unsigned>((total + threads - 1) / threads));
   switch (src_dtype) {
-    case kF32: hipLaunchKernelGGL((write_fp8_kernel<F32S>), grid, dim3(threads), 0, s, a); break;
-    case kF16: hipLaunchKernelGGL((write_fp8_kernel<F16S>), grid, dim3(threads), 0, s, a); break;
-    case kBF16: hipLaunchKernelGGL((write_fp8_kernel<BF16S>), grid, dim3(threads), 0, s, a); break;
+    case kF32: hipLaunchKernelGGL((write_fp8_kernel<F32S>), grid, dim3(threads), 0, s, a, units_log2); break;
+    case kF16: hipLaunchKernelGGL((write_fp8_kernel<F16S>), grid, dim3(threads), 0, s, a, units_log2); break;
+    case kBF16: hipLaunchKernelGGL((write_fp8_kernel<BF16S>), grid, dim3(threads), 0, s, a, units_log2); break;
     default: if (supported) *supported = false; return hipSuccess;
   }
   return hipGetLastError();
