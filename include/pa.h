@@ -126,7 +126,7 @@ int pa_write_kv(const void *k, const void *v, int32_t src_dtype, int32_t num_tok
  * (sequence, query head slot, partition), with
  * ceil(max_blocks_per_seq * block_size / partition_size) partitions per
  * sequence.  With PA_PARTITION_AUTO there are two partials per workgroup the
- * balanced split may launch, 4 per compute unit of the CURRENT device, so
+ * balanced split may launch, 8 per compute unit of the CURRENT device, so
  * size the workspace with the device that will run the call selected.
  * Returns 0 for partition_size == 0 (single pass) and for invalid arguments.
  */

@@ -1127,9 +1127,9 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs a) {
   Fast<QS, KS, GT, BS, 1>::run_stream(a);
 }
 
-// Grid of the balanced split: one single-wave workgroup per SIMD (fewer if
-// this kernel's occupancy is lower), capped by the workspace capacity the
-// caller sized for.
+// Grid of the balanced split: one single-wave workgroup per SIMD for a
+// 16-bit cache, two for fp8 (fewer if this kernel's occupancy is lower),
+// capped by the workspace capacity the caller sized for.
 template <typename QS, typename KS, int GT, int BS>
 hipError_t launch_stream_gt(const DecodeArgs &a, hipStream_t s) {
   static const int per_cu = [] {
@@ -1139,7 +1139,8 @@ hipError_t launch_stream_gt(const DecodeArgs &a, hipStream_t s) {
       n = 8;
     return n;
   }();
-  const int waves = min(a.stream_waves, device_compute_units() * min(per_cu, kMaxStreamWavesPerCu));
+  const int want = std::is_same<KS, FP8S>::value ? kStreamWavesPerCuFp8 : kStreamWavesPerCu16;
+  const int waves = min(a.stream_waves, device_compute_units() * min(per_cu, want));
   hipLaunchKernelGGL((decode_stream_kernel<QS, KS, GT, BS>), dim3(waves), dim3(64), 0, s, a);
   return hipGetLastError();
 }

@@ -86,11 +86,15 @@ inline int device_compute_units() {
   return cus;
 }
 
-// Single-wave workgroups per compute unit that the balanced split launches
-// (its workspace is sized for this many): one per SIMD.  A second wave on a
-// SIMD only gets the issue slots the first leaves over, falls behind it and
-// finishes its share late, with too few loads in flight to keep HBM busy.
-constexpr int kMaxStreamWavesPerCu = 4;
+// Single-wave workgroups per compute unit that the balanced split may
+// launch (its workspace is sized for this many).  A 16-bit cache launches
+// one per SIMD: a second wave on a SIMD only gets the issue slots the first
+// leaves over, falls behind it and finishes its share late.  An fp8 cache
+// carries half the bytes per tile for the same arithmetic, and there two
+// waves per SIMD keep more loads in flight while one of them computes.
+constexpr int kMaxStreamWavesPerCu = 8;
+constexpr int kStreamWavesPerCu16 = 4;
+constexpr int kStreamWavesPerCuFp8 = 8;
 
 // Workspace layout shared by the API layer and the kernels.
 struct WorkspaceLayout {

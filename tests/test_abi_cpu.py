@@ -49,10 +49,10 @@ def test_workspace_bytes():
     assert pa.pa_decode_workspace_bytes(3, 2, 1, 8, 5, 4, 0) == 0
     assert pa.pa_decode_workspace_bytes(0, 2, 1, 8, 5, 4, 8) == 0
     assert pa.pa_decode_workspace_bytes(3, 3, 2, 8, 5, 4, 8) == 0      # heads not a multiple
-    # balanced split: two partials per wave, 4 waves per compute unit (256 CUs
+    # balanced split: two partials per wave, 8 waves per compute unit (256 CUs
     # assumed when no GPU can be queried, as here)
     assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 128, 16, pa.PA_PARTITION_AUTO) == \
-        2048 + 256 * 4 * 2 * 4 * 130 * 4
+        2048 + 256 * 8 * 2 * 4 * 130 * 4
     assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 128, 16, -2) == 0
 
 
