@@ -120,13 +120,13 @@ int pa_write_kv(const void *k, const void *v, int32_t src_dtype, int32_t num_tok
 
 /*
  * pa_decode_workspace_bytes -- device scratch pa_decode needs in split mode:
- * one int32 arrival counter per (sequence, group of up to 8 query heads
+ * one 64-bit arrival counter per (sequence, group of up to 8 query heads
  * sharing a KV head), padded to 256 bytes, then float32 partial maxima, sums
  * and outputs.  With partition_size > 0 there is a partial for every
  * (sequence, query head slot, partition), with
  * ceil(max_blocks_per_seq * block_size / partition_size) partitions per
- * sequence.  With PA_PARTITION_AUTO there are two partials per workgroup the
- * balanced split may launch, 8 per compute unit of the CURRENT device, so
+ * sequence.  With PA_PARTITION_AUTO there are two partials per streaming wave the
+ * balanced split may launch, 4 per compute unit of the CURRENT device, so
  * size the workspace with the device that will run the call selected.
  * Returns 0 for partition_size == 0 (single pass) and for invalid arguments.
  */

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -89,9 +90,13 @@ int heads_per_wg(int group) {
   return h;
 }
 
-// Split-KV scratch: one int32 arrival counter per (sequence, head group),
-// padded to 256 bytes, then float32 partials (m, l and head_dim outputs) for
-// every (sequence, head group, partition, head of the group).
+// Split-KV scratch.
+//  Fixed partitions: one 8-byte arrival counter per (sequence, head group),
+//  padded to 256 bytes, then float32 partials (m, l and head_dim outputs) for
+//  every (sequence, head group, partition, head of the group).
+//  Balanced split: 4 KiB of registration and exit counters, one 128-byte
+//  counter line per (sequence, head group), then two partial slots per range
+//  of every share (one share per XCD, one range per streaming wave).
 bool workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                       int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
                       int32_t partition_size, pa_impl::WorkspaceLayout *w) {
@@ -102,16 +107,18 @@ bool workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_head
   const int group = num_q_heads / num_kv_heads;
   const int hpw = heads_per_wg(group);
   const int64_t hg = ceil_div(group, hpw);
+  *w = pa_impl::WorkspaceLayout{};
   w->units = static_cast<int64_t>(num_seqs) * num_kv_heads * hg;
-  w->counter_bytes = ceil_div(w->units * 4, 256) * 256;
   if (partition_size == PA_PARTITION_AUTO) {
-    // balanced split: at most two partials per launched wave
-    w->stream_waves = static_cast<int64_t>(pa_impl::device_compute_units()) * pa_impl::kMaxStreamWavesPerCu;
-    w->max_parts = 0;
-    w->partial_floats = w->stream_waves * 2 * hpw * (static_cast<int64_t>(head_dim) + 2);
+    w->stream_waves = static_cast<int64_t>(pa_impl::device_compute_units()) * pa_impl::kStreamWavesPerCu;
+    w->num_xcd = std::min(pa_impl::device_xccs(), 16);   // the control block holds 16 registration counters
+    w->share_ranges = pa_impl::kStreamWavesPerCu * ceil_div(w->stream_waves / pa_impl::kStreamWavesPerCu, w->num_xcd);
+    w->ctl_bytes = 4096;
+    w->counter_bytes = w->units * 128;
+    w->partial_floats = w->num_xcd * w->share_ranges * 2 * hpw * (static_cast<int64_t>(head_dim) + 2);
   } else {
-    w->stream_waves = 0;
     w->max_parts = ceil_div(static_cast<int64_t>(max_blocks_per_seq) * block_size, partition_size);
+    w->counter_bytes = ceil_div(w->units * 8, 256) * 256;
     w->partial_floats = w->units * w->max_parts * hpw * (static_cast<int64_t>(head_dim) + 2);
   }
   return true;
@@ -255,10 +262,15 @@ int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
                   workspace ? workspace_bytes : static_cast<size_t>(0));
     a.partition_size = 0;
     a.stream_waves = static_cast<int32_t>(w.stream_waves);
-    a.counters = static_cast<int32_t *>(workspace);
-    float *ws = reinterpret_cast<float *>(static_cast<char *>(workspace) + w.counter_bytes);
-    a.part_o = ws;                                                  // [wave][2][head][D]
-    a.part_m = ws + w.stream_waves * 2 * hpw * pool->head_dim;      // [wave][2][head][m, l]
+    a.num_xcd = static_cast<int32_t>(w.num_xcd);
+    a.share_ranges = static_cast<int32_t>(w.share_ranges);
+    char *base = static_cast<char *>(workspace);
+    a.ctl = reinterpret_cast<int32_t *>(base);
+    a.counters = reinterpret_cast<int32_t *>(base + w.ctl_bytes);
+    float *ws = reinterpret_cast<float *>(base + w.ctl_bytes + w.counter_bytes);
+    const int64_t slots = w.num_xcd * w.share_ranges * 2;
+    a.part_o = ws;                                     // [share][range][side][head][D]
+    a.part_m = ws + slots * hpw * pool->head_dim;      // [share][range][side][head][m, l]
   } else if (partition_size > 0) {
     pa_impl::WorkspaceLayout w{};
     workspace_layout(num_seqs, num_q_heads, pool->num_kv_heads, pool->head_dim, max_blocks_per_seq,

@@ -63,7 +63,6 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kHd = 128;      // head_dim handled here
 constexpr int kTile = 16;     // positions per MFMA tile
-constexpr int kDepth = 4;     // K/V tiles in flight per wave
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
@@ -170,6 +169,39 @@ __device__ __forceinline__ void coherent_wait(T &x) {
   asm volatile("s_waitcnt vmcnt(0)" : "+v"(x) : : "memory");
 }
 
+// The same device-coherent accesses as buffer instructions with the sc1
+// cache-policy bit, which the compiler sees and counts, so it places the
+// waits itself.  `r` is a resource over a whole float array, `off` a byte
+// offset into it (accesses past the array read zeros and write nothing).
+constexpr int kSc1 = 16;                 // cache policy bits: device-coherent scope
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t float_rsrc(const float *base, int64_t count) {
+  const int64_t bytes = count * 4;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), 0,
+                                           static_cast<int>(bytes < 0x7fffffff ? bytes : 0x7fffffff),
+                                           0x00020000);
+}
+__device__ __forceinline__ void rsrc_store4(__amdgpu_buffer_rsrc_t r, int off, f32x4_t v) {
+  typedef uint32_t w4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(w4, v), r, off, 0, kSc1);
+}
+__device__ __forceinline__ void rsrc_store2(__amdgpu_buffer_rsrc_t r, int off, f32x2_t v) {
+  typedef uint32_t w2 __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(w2, v), r, off, 0, kSc1);
+}
+__device__ __forceinline__ f32x4_t rsrc_load4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
+}
+__device__ __forceinline__ f32x2_t rsrc_load2(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kSc1));
+}
+
+// Mailbox flags shared by the waves of a workgroup: volatile LDS accesses
+// (the explicit address space keeps them ds_read / ds_write; a generic
+// volatile access would be a flat access, counted with the K/V loads).
+typedef __attribute__((address_space(3))) volatile int lds_vint_t;
+__device__ __forceinline__ int lds_get(int *p) { return *(lds_vint_t *)(p); }
+__device__ __forceinline__ void lds_put(int *p, int v) { *(lds_vint_t *)(p) = v; }
+
 // One segment's partial for one head: running max m, sum l, and this lane's
 // 8 unnormalised output dims.
 struct Partial {
@@ -253,6 +285,8 @@ struct Fast {
   static constexpr int kRow = kHd * kEsz;              // bytes per K/V row
   static constexpr int kThreads = NW * 64;
   static_assert(BS % kTile == 0, "block size must be a multiple of 16");
+  // K/V tiles in flight per wave (an fp8 tile carries half the bytes)
+  static constexpr int kRing = kFp8 ? 4 : 2;
 
   // first head dim of chunk j's 8-element run for lane group g (A and B agree)
   static __device__ __forceinline__ int dbase(int j, int g) {
@@ -395,8 +429,8 @@ struct Fast {
   // online-softmax state: tile t_first + stride * i for i < count, each 16
   // positions starting at 16 * tile; positions >= pend are masked.
   //
-  // The tiles stream through a ring of kDepth buffers: the loads of tile
-  // i + kDepth are issued as soon as tile i has been computed, so kDepth
+  // The tiles stream through a ring of kRing buffers: the loads of tile
+  // i + kRing are issued as soon as tile i has been computed, so kRing
   // tiles are in flight while one is computed.  Every step issues loads
   // (switched off past the last tile), and a scheduling barrier keeps each
   // buffer's new loads after the compute that frees it, so the buffers stay
@@ -428,13 +462,13 @@ struct Fast {
     for (int e = 0; e < 8; ++e) acc[e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     if (count <= 0) return;
 
-    Tile ring[kDepth];
+    Tile ring[kRing];
 #pragma unroll
-    for (int k = 0; k < kDepth; ++k) issue_tile(ring[k], k, entry(k));
-    int e_next = entry(kDepth);
-    for (int i0 = 0; i0 < count; i0 += kDepth) {
+    for (int k = 0; k < kRing; ++k) issue_tile(ring[k], k, entry(k));
+    int e_next = entry(kRing);
+    for (int i0 = 0; i0 < count; i0 += kRing) {
 #pragma unroll
-      for (int k = 0; k < kDepth; ++k) {
+      for (int k = 0; k < kRing; ++k) {
         const int i = i0 + k;
         if (i < count) {
           if (tpos(i) + kTile <= pend)
@@ -444,8 +478,8 @@ struct Fast {
         }
         __builtin_amdgcn_sched_barrier(0);
         const int e = e_next;
-        e_next = entry(i + kDepth + 1);
-        issue_tile(ring[k], i + kDepth, e);
+        e_next = entry(i + kRing + 1);
+        issue_tile(ring[k], i + kRing, e);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -463,17 +497,22 @@ struct Fast {
     }
   }
 
-  // four consecutive outputs, rounded to the q dtype
-  static __device__ __forceinline__ void store4(const DecodeArgs &a, int64_t idx, float4 o, float mul) {
+  // four outputs rounded to the q dtype, packed in two dwords
+  static __device__ __forceinline__ uint2 pack4(float4 o) {
     uint2 w;
     if constexpr (std::is_same<QS, BF16S>::value) {
-      w.x = f32_to_bf16(o.x * mul) | (static_cast<uint32_t>(f32_to_bf16(o.y * mul)) << 16);
-      w.y = f32_to_bf16(o.z * mul) | (static_cast<uint32_t>(f32_to_bf16(o.w * mul)) << 16);
+      w.x = f32_to_bf16(o.x) | (static_cast<uint32_t>(f32_to_bf16(o.y)) << 16);
+      w.y = f32_to_bf16(o.z) | (static_cast<uint32_t>(f32_to_bf16(o.w)) << 16);
     } else {
-      w.x = f32_to_f16(o.x * mul) | (static_cast<uint32_t>(f32_to_f16(o.y * mul)) << 16);
-      w.y = f32_to_f16(o.z * mul) | (static_cast<uint32_t>(f32_to_f16(o.w * mul)) << 16);
+      w.x = f32_to_f16(o.x) | (static_cast<uint32_t>(f32_to_f16(o.y)) << 16);
+      w.y = f32_to_f16(o.z) | (static_cast<uint32_t>(f32_to_f16(o.w)) << 16);
     }
-    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + idx) = w;
+    return w;
+  }
+  // four consecutive outputs, scaled by mul and rounded to the q dtype
+  static __device__ __forceinline__ void store4(const DecodeArgs &a, int64_t idx, float4 o, float mul) {
+    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + idx) =
+        pack4(make_float4(o.x * mul, o.y * mul, o.z * mul, o.w * mul));
   }
 
   // this lane's 32 output dims (32*g4 .. +31 of head r16), scaled by mul:
@@ -484,6 +523,17 @@ struct Fast {
     for (int r = 0; r < 4; ++r) {
       store4(a, idx + 8 * r, make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]), mul);
       store4(a, idx + 8 * r + 4, make_float4(acc[4][r], acc[5][r], acc[6][r], acc[7][r]), mul);
+    }
+  }
+
+  // store_lane's values into an LDS row (dims 32*g4 .. +31 at dst)
+  static __device__ __forceinline__ void stage_lane(uint16_t *dst, const f32x4_t (&acc)[8], float mul) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float4 lo4 = make_float4(acc[0][r] * mul, acc[1][r] * mul, acc[2][r] * mul, acc[3][r] * mul);
+      const float4 hi4 = make_float4(acc[4][r] * mul, acc[5][r] * mul, acc[6][r] * mul, acc[7][r] * mul);
+      *reinterpret_cast<uint2 *>(dst + 8 * r) = pack4(lo4);
+      *reinterpret_cast<uint2 *>(dst + 8 * r + 4) = pack4(hi4);
     }
   }
 
@@ -536,7 +586,7 @@ struct Fast {
   }
 
   // q staging: 16-byte pieces, piece p = chunk p%16 of head p/16 of the unit
-  static constexpr int kQSlots = 8;
+  static constexpr int kQSlots = 4;
   static constexpr int kQPieces = (GT * 16 + 63) / 64;
   static __device__ __forceinline__ uint4 q_piece(const DecodeArgs &a, int s, int u, int p) {
     const int kvh = u / a.head_groups;
@@ -557,10 +607,13 @@ struct Fast {
     }
   }
 
-  // floor(a / b) for 0 <= a < 2^53 and 0 < b < 2^31: the double quotient is
-  // within one of the exact one, and one integer check on each side fixes
-  // it (a 64-bit integer division is a long instruction sequence here)
+  // floor(a / b) for 0 <= a < 2^53 and 0 < b < 2^31.  Operands below 2^32
+  // take the 32-bit integer division; larger ones the double quotient, which
+  // is within one of the exact one, corrected by one integer check on each
+  // side (a 64-bit integer division is a long instruction sequence here)
   static __device__ __forceinline__ int64_t floor_div(int64_t a, int64_t b) {
+    if (((static_cast<uint64_t>(a) | static_cast<uint64_t>(b)) >> 32) == 0)
+      return static_cast<uint32_t>(a) / static_cast<uint32_t>(b);
     int64_t q = static_cast<int64_t>(static_cast<double>(a) / static_cast<double>(b));
     if (q * b > a)
       --q;
@@ -568,33 +621,97 @@ struct Fast {
       ++q;
     return q;
   }
-  // first tile of range w (T * W < 2^53, i.e. fewer than 2^40 tiles)
-  static __device__ __forceinline__ int64_t range_lo(int64_t T, int64_t W, int64_t w) {
-    return floor_div(T * w, W);
+  // first tile of part x when T tiles are cut into W near-equal parts
+  // (T * W < 2^53, i.e. fewer than 2^40 tiles)
+  static __device__ __forceinline__ int64_t range_lo(int64_t T, int64_t W, int64_t x) {
+    return floor_div(T * x, W);
   }
-  // wave whose tile range holds global tile g (T >= W >= 1, so no range is
-  // empty): the last w with floor(T w / W) <= g, i.e. floor(((g+1) W - 1) / T);
-  // g is clamped into [0, T) first
-  static __device__ __forceinline__ int64_t wave_of(int64_t T, int64_t W, int64_t g) {
+  // the part holding tile g (0 <= g < T): the last x with range_lo(x) <= g,
+  // i.e. floor(((g+1) W - 1) / T); parts may be empty when T < W
+  static __device__ __forceinline__ int64_t part_of(int64_t T, int64_t W, int64_t g) {
     g = min(max(g, static_cast<int64_t>(0)), T - 1);
     return min(floor_div((g + 1) * W - 1, T), W - 1);
   }
 
-  static __device__ void run_stream(const DecodeArgs &a) {
-    const int64_t w = blockIdx.x;
-    const int lane = threadIdx.x;
+  // -------------------------------------------------------------------------
+  // Balanced split: XCD shares, static ranges, paired waves.
+  //
+  // Work.  The batch's work is the list of 16-position tiles of every
+  // (sequence, head group) unit, units ordered by sequence then head group,
+  // T tiles in all.  It is cut into one contiguous share per XCD, and share x
+  // into 4 * n(x) near-equal ranges, one per streaming wave, where n(x) is
+  // the number of workgroups the dispatcher places on XCD x (it deals
+  // workgroups to the XCDs in turn, so n(x) = ceil((grid - x) / XCDs)).  A
+  // workgroup reads its XCD from the hardware and takes the next index on
+  // that XCD's registration counter; its four streamers take the ranges
+  // 4 * index .. 4 * index + 3 of the share.  Range boundaries depend on T
+  // and the grid only, so a split unit's partials and their merge order do
+  // not depend on timing: the output is bit-identical from run to run.
+  //
+  // Waves.  A workgroup of 8 waves holds 4 streaming waves (0..3, one per
+  // SIMD) and 4 helper waves (helper i + 4 shares streamer i's SIMD and
+  // serves it).  A streamer issues only K/V, q and table loads: a global
+  // store issued between the K/V loads would hold up the counting of every
+  // load issued after it until it is acknowledged.  Each finished segment (a
+  // whole unit's outputs, or a range's partial for a unit split between
+  // ranges) goes to the helper through an LDS mailbox; the helper writes the
+  // rows, publishes the partials, counts them in and merges the split units
+  // while its streamer keeps streaming.
+  //
+  // Exchange.  The partials of a unit inside one share are written and
+  // merged by waves of one XCD, so they go through that XCD's L2 with
+  // ordinary stores and loads that only skip the compute unit's L1 (a
+  // device-coherent store is written through to memory and slows every
+  // wave's K/V loads down).  A unit that crosses a share boundary (at most
+  // one per boundary) uses device-coherent stores and loads.  The counters
+  // are device-scope atomics either way.
+  //
+  // Check.  The grid's last helper compares every XCD's registration count
+  // with n(x); if the dispatcher placed the workgroups otherwise, some
+  // ranges were not streamed, and it turns every output row into NaN
+  // rather than leave rows unwritten.  It then resets the counters.
+  // -------------------------------------------------------------------------
+
+  // workgroups the dispatcher places on XCD x, and share x's tiles and ranges
+  static __device__ __forceinline__ int64_t wgs_on(int64_t x, int NX) {
+    return (static_cast<int64_t>(gridDim.x) - x + NX - 1) / NX;
+  }
+  struct Share {
+    int64_t X0, X1, nr;   // tiles [X0, X1) in nr ranges
+  };
+  static __device__ __forceinline__ Share share_geom(int64_t T, int NX, int64_t x) {
+    return Share{range_lo(T, NX, x), range_lo(T, NX, x + 1), 4 * wgs_on(x, NX)};
+  }
+  static __device__ __forceinline__ void range_of(const Share &sh, int64_t i, int64_t &lo, int64_t &hi) {
+    const int64_t L = sh.X1 - sh.X0;
+    lo = sh.X0 + range_lo(L, sh.nr, i);
+    hi = sh.X0 + range_lo(L, sh.nr, i + 1);
+  }
+
+  // One finished segment in the mailbox: unnormalised outputs o (head h,
+  // dims 4*d4 .. +3 at o[h * 32 + d4]), per head (m, l), and where it belongs.
+  static constexpr int kMail = 4;
+  struct Mail {
+    f32x4_t o[GT * (kHd / 4)];
+    f32x2_t ml[GT];
+    int64_t unit, gu, row0;
+    int nts, hcount, split, side;
+  };
+  struct Box {
+    Mail m[kMail];
+    int head, tail, done, pad;     // posted (streamer), taken (helper); streamer finished
+  };
+
+  // total tiles T of the batch; n_lane / cnt0 / incl0: the first 64
+  // sequences' lengths, tile counts and inclusive running sums, one per lane
+  static __device__ __forceinline__ int64_t count_tiles(const DecodeArgs &a, int lane, int &n_lane,
+                                                        int64_t &cnt0, int64_t &incl0) {
     const int S = a.num_seqs;
     const int KVG = a.num_kv_heads * a.head_groups;
     const int maxn = a.max_blocks * BS;
-    const float nanv = __builtin_nanf("");
-    auto tiles_of = [&](int n) { return (n > 0 && n <= maxn) ? (n + kTile - 1) / kTile : 0; };
-
-    // total tiles, then the sequence holding this wave's first tile; the
-    // first 64 lengths stay in registers, so for up to 64 sequences one load
-    // serves both steps
-    const int n_lane = lane < S ? a.ctx[lane] : 0;
-    const int64_t cnt0 = tiles_of(n_lane);
-    int64_t incl0 = cnt0;
+    n_lane = lane < S ? a.ctx[lane] : 0;
+    cnt0 = tiles_of(n_lane, maxn);
+    incl0 = cnt0;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int64_t up = __shfl_up(incl0, o, 64);
@@ -602,86 +719,159 @@ struct Fast {
     }
     int64_t T = uniform(__shfl(incl0, 63, 64));
     for (int c0 = 64; c0 < S; c0 += 64) {
-      int64_t cnt = (c0 + lane < S) ? tiles_of(a.ctx[c0 + lane]) : 0;
+      int64_t cnt = (c0 + lane < S) ? tiles_of(a.ctx[c0 + lane], maxn) : 0;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) cnt += __shfl_xor(cnt, o, 64);
       T += cnt;
     }
-    T = uniform(T * KVG);
-    // the work is cut into min(grid, T) ranges, so every range holds at least
-    // one tile (an empty range would never count its partial in); the waves
-    // past that have nothing to do
-    const int64_t W = min(static_cast<int64_t>(gridDim.x), T);
-    const int64_t lo = w < W ? range_lo(T, W, w) : 0;
-    const int64_t hi = w < W ? range_lo(T, W, w + 1) : 0;
-    if (lo < hi) stream(a, T, W, w, lo, hi, n_lane, cnt0, incl0);
-
-    // rows of empty (zero) and out-of-range (NaN) sequences
-    for (int s = static_cast<int>(w); s < S; s += static_cast<int>(gridDim.x)) {
-      const int n = load_const(a.ctx, s);
-      if (n > 0 && n <= maxn) continue;
-      const float fill = n == 0 ? 0.0f : nanv;
-      for (int i = lane; i < a.num_q_heads * (kHd / 4); i += 64)
-        store4(a, (static_cast<int64_t>(s) * a.num_q_heads + (i >> 5)) * kHd + 4 * (i & 31),
-               make_float4(fill, fill, fill, fill), 1.0f);
-    }
+    return uniform(T * KVG);
   }
 
-  // The wave's tile range [lo, hi) of the T-tile list cut into W ranges.
-  // n_lane / cnt0 / incl0: the first 64 sequences' lengths, tile counts and
-  // their inclusive running sum, one per lane.
-  static __device__ void stream(const DecodeArgs &a, int64_t T, int64_t W, int64_t w, int64_t lo,
-                                int64_t hi, int n_lane, int64_t cnt0, int64_t incl0) {
-    const int lane = threadIdx.x;
-    const int r16 = lane & 15;
-    const int g4 = lane >> 4;
+  // the list position of global tile g (0 <= g < T)
+  static __device__ Cursor locate(const DecodeArgs &a, int64_t g, int lane, int n_lane, int64_t cnt0,
+                                  int64_t incl0) {
     const int S = a.num_seqs;
     const int KVG = a.num_kv_heads * a.head_groups;
     const int maxn = a.max_blocks * BS;
-    const float nanv = __builtin_nanf("");
-    auto tiles_of = [&](int n) { return (n > 0 && n <= maxn) ? (n + kTile - 1) / kTile : 0; };
-
     int s = 0, n0 = 0;
     int64_t G = 0;                     // first global tile of sequence s
-    {
-      const int64_t total0 = uniform(__shfl(incl0, 63, 64)) * KVG;
-      if (total0 > lo) {
-        const int first = __builtin_ctzll(__builtin_amdgcn_ballot_w64(incl0 * KVG > lo));
-        s = uniform(first);
-        G = uniform((__shfl(incl0, first, 64) - __shfl(cnt0, first, 64)) * KVG);
-        n0 = __builtin_amdgcn_readlane(n_lane, first);
-      } else {
-        int64_t base = total0;
-        for (int c0 = 64; c0 < S; c0 += 64) {
-          const int64_t cnt = ((c0 + lane < S) ? tiles_of(a.ctx[c0 + lane]) : 0) * static_cast<int64_t>(KVG);
-          int64_t incl = cnt;
+    const int64_t total0 = uniform(__shfl(incl0, 63, 64)) * KVG;
+    if (total0 > g) {
+      const int first = __builtin_ctzll(__builtin_amdgcn_ballot_w64(incl0 * KVG > g));
+      s = uniform(first);
+      G = uniform((__shfl(incl0, first, 64) - __shfl(cnt0, first, 64)) * KVG);
+      n0 = __builtin_amdgcn_readlane(n_lane, first);
+    } else {
+      int64_t base = total0;
+      for (int c0 = 64; c0 < S; c0 += 64) {
+        const int64_t cnt = ((c0 + lane < S) ? tiles_of(a.ctx[c0 + lane], maxn) : 0) * static_cast<int64_t>(KVG);
+        int64_t incl = cnt;
 #pragma unroll
-          for (int o = 1; o < 64; o <<= 1) {
-            const int64_t up = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += up;
-          }
-          const int64_t total = uniform(__shfl(incl, 63, 64));
-          if (base + total > lo) {
-            const int first = __builtin_ctzll(__builtin_amdgcn_ballot_w64(base + incl > lo));
-            s = uniform(c0 + first);
-            G = uniform(base + __shfl(incl, first, 64) - __shfl(cnt, first, 64));
-            n0 = load_const(a.ctx, s);
-            break;
-          }
-          base += total;
+        for (int o = 1; o < 64; o <<= 1) {
+          const int64_t up = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += up;
         }
+        const int64_t total = uniform(__shfl(incl, 63, 64));
+        if (base + total > g) {
+          const int first = __builtin_ctzll(__builtin_amdgcn_ballot_w64(base + incl > g));
+          s = uniform(c0 + first);
+          G = uniform(base + __shfl(incl, first, 64) - __shfl(cnt, first, 64));
+          n0 = load_const(a.ctx, s);
+          break;
+        }
+        base += total;
       }
     }
-    Cursor c0;
-    c0.s = s;
-    c0.n = n0;
-    c0.nts = tiles_of(c0.n);
-    c0.u = static_cast<int>(floor_div(lo - G, c0.nts));
-    c0.t = static_cast<int>(lo - G - static_cast<int64_t>(c0.u) * c0.nts);
-    c0.G = G;
+    Cursor c;
+    c.s = s;
+    c.n = n0;
+    c.nts = tiles_of(n0, maxn);
+    c.u = static_cast<int>(floor_div(g - G, c.nts));
+    c.t = static_cast<int>(g - G - static_cast<int64_t>(c.u) * c.nts);
+    c.G = G;
+    return c;
+  }
+
+  // Workspace control words, one 128-byte line each: the count of finished
+  // workgroup groups at ctl[0], XCD x's registration count at
+  // ctl[32 * (1 + x)] (x < 16), workgroup group g's count of finished
+  // workgroups at ctl[32 * (17 + g)] (g < 8); the unit counters at
+  // a.counters + 32 * unit (one 128-byte line each, 64-bit).
+  static __device__ __forceinline__ int *reg_ctr(const DecodeArgs &a, int64_t x) { return a.ctl + 32 * (x + 1); }
+  static __device__ __forceinline__ int *group_ctr(const DecodeArgs &a, int64_t g) { return a.ctl + 32 * (17 + g); }
+  static __device__ __forceinline__ uint64_t *unit_ctr(const DecodeArgs &a, int64_t unit) {
+    return reinterpret_cast<uint64_t *>(a.counters) + 16 * unit;
+  }
+
+  static __device__ void run_pair(const DecodeArgs &a) {
+    __shared__ Box box[4];
+    __shared__ uint4 s_q[4][kQSlots][GT * 16];
+    __shared__ int s_reg, s_exit, s_tbl;
+    // dynamic LDS: the table of range starts (the helpers' lookups)
+    extern __shared__ int64_t pa_dyn_lds[];
+    const int wave = uniform(static_cast<int>(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    const int slot = wave & 3;
+    const bool helper = wave >= 4;
+    Box &bx = box[slot];
+    // this workgroup's XCD selects its share (the exchange of a share's
+    // partials relies on all its waves sharing one L2)
+    const int NX = a.num_xcd;
+    const int64_t x = static_cast<int64_t>(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15) % NX;
+    if (threadIdx.x == 0) {
+      s_reg = __hip_atomic_fetch_add(reg_ctr(a, x), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_exit = 0;
+      s_tbl = 0;
+    }
+    if (lane == 0) {
+      if (helper) {
+        bx.tail = 0;
+      } else {
+        bx.head = 0;
+        bx.done = 0;
+      }
+    }
+    __syncthreads();
+    const int64_t reg = s_reg;
+
+    int n_lane;
+    int64_t cnt0, incl0;
+    const int64_t T = count_tiles(a, lane, n_lane, cnt0, incl0);
+    const Share sh = share_geom(T, NX, x);
+    if (!helper) {
+      if (reg < wgs_on(x, NX)) {
+        int64_t lo, hi;
+        range_of(sh, 4 * reg + slot, lo, hi);
+        if (lo < hi) stream(a, bx, s_q[slot], lo, hi, lane, n_lane, cnt0, incl0);
+      }
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (lane == 0) lds_put(&bx.done, 1);
+      return;
+    }
+    // The helpers fill the table of range starts: rs[r] for the batch's
+    // ranges in tile order (r < NR, share by share), rs[NR] = T, and for
+    // each range its share y and index i in the share, as (y << 20) | i.
+    const int64_t NR = 4 * static_cast<int64_t>(gridDim.x);
+    int64_t *rs = pa_dyn_lds;
+    int *rc = reinterpret_cast<int *>(pa_dyn_lds + NR + 1);
+    {
+      const int64_t q = static_cast<int64_t>(gridDim.x) / NX, rr = static_cast<int64_t>(gridDim.x) - q * NX;
+      for (int64_t r = (wave - 4) * 64 + lane; r <= NR; r += 256) {
+        if (r == NR) {
+          rs[r] = T;
+          continue;
+        }
+        int64_t y = 0, cum = 0;
+        while (cum + 4 * (q + (y < rr ? 1 : 0)) <= r) cum += 4 * (q + (y++ < rr ? 1 : 0));
+        const int64_t i = r - cum;
+        const Share sy = share_geom(T, NX, y);
+        int64_t lo, hi;
+        range_of(sy, i, lo, hi);
+        rs[r] = lo;
+        rc[r] = static_cast<int>((y << 20) | i);
+      }
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (lane == 0) __hip_atomic_fetch_add(&s_tbl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      while (lds_get(&s_tbl) < 4) __builtin_amdgcn_s_sleep(1);   // the four helpers have filled it
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
+    helper_main(a, bx, T, x, x * (a.share_ranges) + 4 * reg + slot, lane, s_exit, rs, rc);
+  }
+
+  // The streamer's tile range [lo, hi) of the T-tile list.  Finished
+  // segments go to the mailbox `bx`; `sq` stages q of the range's first
+  // kQSlots units.
+  static __device__ void stream(const DecodeArgs &a, Box &bx, uint4 (*sq)[GT * 16], int64_t lo, int64_t hi,
+                                int lane, int n_lane, int64_t cnt0, int64_t incl0) {
+    const int r16 = lane & 15;
+    const int g4 = lane >> 4;
+    const int KVG = a.num_kv_heads * a.head_groups;
+    const int maxn = a.max_blocks * BS;
+    const float nanv = __builtin_nanf("");
+    const Cursor c0 = locate(a, lo, lane, n_lane, cnt0, incl0);
 
     // Set-up order: the first table entry, the q loads, then the first
-    // kDepth tiles' loads, and only then the q stores to LDS (whose wait for
+    // kRing tiles' loads, and only then the q stores to LDS (whose wait for
     // the q loads leaves the tile loads in flight).
     const int ko = k_lane_offset(r16, g4), vo = v_lane_offset(r16, g4);
     const int64_t head_bytes = static_cast<int64_t>(BS) * kRow;
@@ -699,10 +889,6 @@ struct Fast {
     // q of the range's first kQSlots units, staged in LDS, so that starting
     // a unit mid-stream never waits on a global load (that wait would also
     // wait for every K/V load issued before it)
-    __shared__ uint4 s_q[kQSlots][GT * 16];
-    // the range's (at most two) partials, kept here until the stream is done
-    __shared__ f32x4_t s_po[2][GT * (kHd / 4)];
-    __shared__ f32x2_t s_pml[2][GT];
     uint4 qv[kQSlots][kQPieces];
     int nq = 0;
     {
@@ -721,7 +907,7 @@ struct Fast {
       }
     }
 
-    // One pipeline over the whole range: the issue cursor runs kDepth tiles
+    // One pipeline over the whole range: the issue cursor runs kRing tiles
     // ahead of the compute cursor and crosses unit boundaries freely, so
     // the K/V stream never drains between units.
     auto issue_next = [&](Tile &tile, int k) {
@@ -741,47 +927,42 @@ struct Fast {
       issue(tile, kpool, vpool, off, on, ko, vo);
     };
 
-    Tile ring[kDepth];
+    Tile ring[kRing];
 #pragma unroll
-    for (int k = 0; k < kDepth; ++k) issue_next(ring[k], k);
+    for (int k = 0; k < kRing; ++k) issue_next(ring[k], k);
 
 #pragma unroll
     for (int k = 0; k < kQSlots; ++k)
       if (k < nq)
 #pragma unroll
         for (int i = 0; i < kQPieces; ++i)
-          if (lane + 64 * i < GT * 16) s_q[k][lane + 64 * i] = qv[k][i];
-    __syncthreads();
+          if (lane + 64 * i < GT * 16) sq[k][lane + 64 * i] = qv[k][i];
 
     Cursor cc = c0;                    // compute cursor
     int64_t gc = lo;
     int nseg = 0;                      // segments started (q slot index)
     int64_t seg_g0 = lo;
-    int seg_t0 = c0.t;
     int hcount = 0;
     int64_t row0 = 0;
     float m_run = -INFINITY, l_run = 0.0f;
     f32x4_t acc[8];
     V8 qb[4];
     bool bad = false;
-    // the range's split units (slot 0: its first unit, slot 1: its last),
-    // whose partials are counted in once the stream is done
-    Split sp0 = {}, sp1 = {};
+    int head = 0, tail_seen = 0;       // mailbox entries posted / known to be free
 
-    for (int64_t g0 = lo; g0 < hi; g0 += kDepth) {
+    for (int64_t g0 = lo; g0 < hi; g0 += kRing) {
 #pragma unroll
-      for (int k = 0; k < kDepth; ++k) {
+      for (int k = 0; k < kRing; ++k) {
         if (gc < hi) {
           if (gc == lo || cc.t == 0) {
             // a segment (the part of a unit inside the range) starts
             seg_g0 = gc;
-            seg_t0 = cc.t;
             const int kvh = cc.u / a.head_groups;
             const int hg = cc.u - kvh * a.head_groups;
             hcount = min(GT, a.group - hg * GT);
             row0 = static_cast<int64_t>(cc.s) * a.num_q_heads + kvh * a.group + hg * GT;
             if (nseg < kQSlots) {
-              q_from_lds(s_q[nseg], hcount, r16, g4, qb);
+              q_from_lds(sq[nseg], hcount, r16, g4, qb);
             } else {
               // past the staged units (very short contexts): a direct load,
               // waited for here so no pending load leaks into the stream
@@ -803,35 +984,41 @@ struct Fast {
           bad |= ((slot_bad >> k) & 1u) != 0;
 
           if (gc == hi - 1 || cc.t == cc.nts - 1) {
-            // the segment ends: the output rows if it is the whole unit, else
-            // this range's partial for the unit (published without waiting)
+            // the segment ends: a whole unit's outputs or this range's
+            // partial for a split unit, handed to the helper
             const float l = xor32_sum(xor16_sum(l_run));
-            if (seg_t0 == 0 && cc.t == cc.nts - 1) {
-              if (r16 < hcount)
-                store_lane(a, (row0 + r16) * kHd + 32 * g4, acc, bad ? nanv : a.v_scale / l);
-            } else {
-              // (written to global memory only after the stream: stores
-              // written through to the device-coherent level while the K/V
-              // loads stream slow the whole stream down)
-              const int slot = seg_g0 == lo ? 0 : 1;
-              const float mul = bad ? nanv : 1.0f;
-              if (r16 < GT) {
-                f32x4_t *dst = &s_po[slot][r16 * (kHd / 4) + 8 * g4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                  dst[2 * r] = f32x4_t{acc[0][r], acc[1][r], acc[2][r], acc[3][r]} * mul;
-                  dst[2 * r + 1] = f32x4_t{acc[4][r], acc[5][r], acc[6][r], acc[7][r]} * mul;
-                }
-                if (g4 == 0) s_pml[slot][r16] = f32x2_t{bad ? nanv : m_run, bad ? nanv : l};
+            if (head - tail_seen >= kMail) {
+              for (;;) {
+                tail_seen = lds_get(&bx.tail);
+                if (head - tail_seen < kMail) break;
+                __builtin_amdgcn_s_sleep(1);
               }
-              Split &sp = slot == 0 ? sp0 : sp1;
-              sp.on = true;
-              sp.unit = static_cast<int64_t>(cc.s) * KVG + cc.u;
-              sp.gu = cc.G + static_cast<int64_t>(cc.u) * cc.nts;
-              sp.nts = cc.nts;
-              sp.hcount = hcount;
-              sp.row0 = row0;
+              __atomic_signal_fence(__ATOMIC_SEQ_CST);
             }
+            Mail &e = bx.m[head % kMail];
+            const float mul = bad ? nanv : 1.0f;
+            if (r16 < GT) {
+              f32x4_t *dst = &e.o[r16 * (kHd / 4) + 8 * g4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                dst[2 * r] = f32x4_t{acc[0][r], acc[1][r], acc[2][r], acc[3][r]} * mul;
+                dst[2 * r + 1] = f32x4_t{acc[4][r], acc[5][r], acc[6][r], acc[7][r]} * mul;
+              }
+              if (g4 == 0) e.ml[r16] = f32x2_t{bad ? nanv : m_run, bad ? nanv : l};
+            }
+            if (lane == 0) {
+              const int64_t gu = cc.G + static_cast<int64_t>(cc.u) * cc.nts;
+              e.split = !(seg_g0 == gu && cc.t == cc.nts - 1);
+              e.side = seg_g0 == lo ? 0 : 1;
+              e.unit = static_cast<int64_t>(cc.s) * KVG + cc.u;
+              e.gu = gu;
+              e.nts = cc.nts;
+              e.hcount = hcount;
+              e.row0 = row0;
+            }
+            ++head;
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (lane == 0) lds_put(&bx.head, head);
           }
           advance(a, cc, KVG, maxn, n_lane);
           ++gc;
@@ -841,129 +1028,185 @@ struct Fast {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-
-    // Publish the partials (device-coherent stores), wait until they have
-    // landed, count them in, and merge every unit whose last partial this was.
-    __syncthreads();
-    if (sp0.on) publish(a, w, 0, s_po[0], s_pml[0], lane);
-    if (sp1.on) publish(a, w, 1, s_po[1], s_pml[1], lane);
-    __builtin_amdgcn_s_waitcnt(0x0f70);      // vmcnt(0)
-    int last0 = 0, last1 = 0;
-    if (lane == 0) {
-      if (sp0.on)
-        last0 = __hip_atomic_fetch_add(a.counters + sp0.unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (sp1.on)
-        last1 = __hip_atomic_fetch_add(a.counters + sp1.unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    // the unit's first and last range (worked out while the atomics fly)
-    if (sp0.on) {
-      sp0.wf = wave_of(T, W, sp0.gu);
-      sp0.wl = wave_of(T, W, sp0.gu + sp0.nts - 1);
-    }
-    if (sp1.on) {
-      sp1.wf = wave_of(T, W, sp1.gu);
-      sp1.wl = wave_of(T, W, sp1.gu + sp1.nts - 1);
-    }
-    sp0.on = sp0.on && __builtin_amdgcn_readlane(last0, 0) == static_cast<int>(sp0.wl - sp0.wf);
-    sp1.on = sp1.on && __builtin_amdgcn_readlane(last1, 0) == static_cast<int>(sp1.wl - sp1.wf);
-    if (sp0.on || sp1.on) merge_units(a, T, W, sp0, sp1, r16, g4);
   }
 
-  // write one of this range's partials from LDS to its global slot
-  static __device__ __forceinline__ void publish(const DecodeArgs &a, int64_t w, int slot, const f32x4_t *po,
-                                                 const f32x2_t *pml, int lane) {
-    float *go = a.part_o + (w * 2 + slot) * (GT * kHd);
-    float *gml = a.part_m + (w * 2 + slot) * (GT * 2);
-#pragma unroll
-    for (int i = lane; i < GT * (kHd / 4); i += 64) coherent_store4(go + 4 * i, po[i]);
-    if (lane < GT) {
-      coherent_store(gml + 2 * lane, pml[lane][0]);
-      coherent_store(gml + 2 * lane + 1, pml[lane][1]);
+  // The helper of the streamer with range index `rid` (share * share_ranges
+  // + range): first the rows of empty (zero) and out-of-range (NaN)
+  // sequences, then the mailbox until the streamer is done, then the exit
+  // count.
+  static __device__ void helper_main(const DecodeArgs &a, Box &bx, int64_t T, int64_t x, int64_t rid, int lane,
+                                     int &s_exit, const int64_t *rs, const int *rc) {
+    const int NX = a.num_xcd;
+    const int64_t nh = 4 * static_cast<int64_t>(gridDim.x);
+    const int maxn = a.max_blocks * BS;
+    const int hid = static_cast<int>(threadIdx.x >> 6) - 4;
+    for (int s = hid * static_cast<int>(gridDim.x) + static_cast<int>(blockIdx.x); s < a.num_seqs;
+         s += static_cast<int>(nh)) {
+      const int n = load_const(a.ctx, s);
+      if (n > 0 && n <= maxn) continue;
+      const float fill = n == 0 ? 0.0f : __builtin_nanf("");
+      for (int i = lane; i < a.num_q_heads * (kHd / 4); i += 64)
+        store4(a, (static_cast<int64_t>(s) * a.num_q_heads + (i >> 5)) * kHd + 4 * (i & 31),
+               make_float4(fill, fill, fill, fill), 1.0f);
+    }
+
+    int tail = 0;
+    for (;;) {
+      const int done = lds_get(&bx.done);
+      const int head = lds_get(&bx.head);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (tail < head) {
+        handle(a, T, rid, bx.m[tail % kMail], lane, rs, rc);
+        ++tail;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane == 0) lds_put(&bx.tail, tail);
+        continue;
+      }
+      if (done) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+
+    // The grid's last helper checks the registrations and resets the
+    // counters.  It is found in three steps, so that no counter takes more
+    // than a few dozen atomics: the workgroup's last helper (LDS), the last
+    // workgroup of its group (workgroups b with b % 8 == g), the last group.
+    __builtin_amdgcn_s_waitcnt(0x0f70);        // vmcnt(0): this helper's stores have landed
+    int last = 0;
+    if (lane == 0) last = __hip_atomic_fetch_add(&s_exit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 3;
+    if (!uniform(last)) return;
+    const int g = blockIdx.x & 7;
+    const int in_group = (static_cast<int>(gridDim.x) - g + 7) >> 3;
+    const int groups = min(8, static_cast<int>(gridDim.x));
+    if (lane == 0)
+      last = __hip_atomic_fetch_add(group_ctr(a, g), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == in_group - 1;
+    if (!uniform(last)) return;
+    if (lane == 0) last = __hip_atomic_fetch_add(a.ctl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == groups - 1;
+    if (!uniform(last)) return;
+    bool missing = false;
+    if (lane < NX) {
+      missing = __hip_atomic_load(reg_ctr(a, lane), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
+                wgs_on(lane, NX);
+      __hip_atomic_store(reg_ctr(a, lane), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (lane < 8) __hip_atomic_store(group_ctr(a, lane), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) __hip_atomic_store(a.ctl, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__builtin_amdgcn_ballot_w64(missing) != 0) {
+      const float nanv = __builtin_nanf("");
+      const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;
+      for (int64_t i = lane; i < rows * (kHd / 4); i += 64)
+        store4(a, 4 * i, make_float4(nanv, nanv, nanv, nanv), 1.0f);
     }
   }
 
-  // One split unit of a range: its global index, first global tile, tile
-  // count, head count, first output row, and the first and last range that
-  // hold part of it (wl - wf + 1 partials).
-  struct Split {
-    bool on;
-    int64_t unit, gu, row0, wf, wl;
-    int nts, hcount;
-  };
+  // The helper's work for one mailbox entry of the streamer with range index
+  // `rid`.  A whole unit: its output rows.  A split unit: the range's partial
+  // is published (partial slot (range index, side); side 1 when the range
+  // began before the unit), then counted in on the unit's counter; the count
+  // that reaches the number of ranges holding the unit merges their partials
+  // in tile order (this one straight from LDS), writes the rows and resets
+  // the counter to zero.
+  static __device__ void handle(const DecodeArgs &a, int64_t T, int64_t rid, const Mail &e, int lane,
+                                const int64_t *rs, const int *rc) {
+    const int NX = a.num_xcd;
+    const int hc = e.hcount;
+    const int64_t row0 = e.row0;
+    if (!e.split) {
+      for (int i = lane; i < hc * (kHd / 4); i += 64) {
+        const int h = i >> 5;
+        const f32x4_t o = e.o[i];
+        store4(a, (row0 + h) * kHd + 4 * (i & 31), make_float4(o[0], o[1], o[2], o[3]), a.v_scale / e.ml[h][1]);
+      }
+      return;
+    }
+    const int64_t gu = e.gu, glast = e.gu + e.nts - 1;
+    const int64_t sr = a.share_ranges;
+    const int64_t NR = 4 * static_cast<int64_t>(gridDim.x);
+    // the range holding gu (ranges are near-equal, so the proportional guess
+    // is a step or two away), then the non-empty ranges up to glast
+    int64_t r1 = min(NR - 1, static_cast<int64_t>(static_cast<float>(gu) * static_cast<float>(NR) /
+                                                  static_cast<float>(T)));
+    while (rs[r1] > gu) --r1;
+    while (rs[r1 + 1] <= gu) ++r1;
+    int64_t count = 1, rl = r1;
+    for (int64_t j = r1 + 1; j < NR && rs[j] <= glast; ++j)
+      if (rs[j + 1] > rs[j]) {
+        ++count;
+        rl = j;
+      }
+    const bool cross = (rc[r1] >> 20) != (rc[rl] >> 20);
+    // partial slot of range j for this unit
+    auto slot_of = [&](int64_t j) {
+      return ((rc[j] >> 20) * sr + (rc[j] & 0xfffff)) * 2 + (rs[j] < gu ? 1 : 0);
+    };
+    const auto ro = float_rsrc(a.part_o, NX * sr * 2 * GT * kHd);
+    const auto rm = float_rsrc(a.part_m, NX * sr * 2 * GT * 2);
+    const int own = static_cast<int>(rid * 2 + e.side);
+    if (cross) {
+      for (int i = lane; i < GT * (kHd / 4); i += 64) rsrc_store4(ro, (own * (GT * kHd) + 4 * i) * 4, e.o[i]);
+      if (lane < GT) rsrc_store2(rm, (own * GT + lane) * 8, e.ml[lane]);
+    } else {
+      typedef uint32_t w4 __attribute__((ext_vector_type(4)));
+      typedef uint32_t w2 __attribute__((ext_vector_type(2)));
+      for (int i = lane; i < GT * (kHd / 4); i += 64)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(w4, e.o[i]), ro, (own * (GT * kHd) + 4 * i) * 4, 0, 0);
+      if (lane < GT) __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(w2, e.ml[lane]), rm, (own * GT + lane) * 8, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);        // vmcnt(0): published before counted
+    uint64_t *ctr = unit_ctr(a, e.unit);
+    uint64_t old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(ctr, uint64_t{1}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (uniform(static_cast<int64_t>(old)) != count - 1) return;
 
-  // Merge the partials of up to two units (those with .on) in range order
-  // and write their output rows.  Row g4 of the wave merges heads g4, g4+4,
-  // ... of both units at once, four partials' loads in flight per unit.  A
-  // range's partial sits in its first slot unless the range began inside
-  // the unit's predecessor.  Leaves the units' counters at zero.
-  static __device__ void merge_units(const DecodeArgs &a, int64_t T, int64_t W, const Split &sp0,
-                                     const Split &sp1, int r16, int g4) {
+    // the last count: fold the unit's partials in tile order, eight loads in
+    // flight at a time
     const float nanv = __builtin_nanf("");
-    struct U {
-      bool on;
-      int64_t wf, wl, wsplit;
-    } u[2];
-    const Split *sp[2] = {&sp0, &sp1};
+    const int r16 = lane & 15, g4 = lane >> 4;
+    for (int h = g4; h < hc; h += 4) {
+      float big_m = -INFINITY, l = 0.0f;
+      float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      bool nan_seen = false;
+      int64_t jr = r1;                 // next range to fold
+      for (int64_t done = 0; done < count;) {
+        Partial p[8];
+        bool live[8];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      u[k] = U{false, 0, 0, 0};
-      if (sp[k]->on) {
-        u[k].on = true;
-        u[k].wf = sp[k]->wf;
-        u[k].wl = sp[k]->wl;
-        u[k].wsplit = u[k].wf + (range_lo(T, W, u[k].wf) < sp[k]->gu ? 1 : 0);
-      }
-    }
-    const int hmax = max(sp0.on ? sp0.hcount : 0, sp1.on ? sp1.hcount : 0);
-    for (int h = g4; h < hmax; h += 4) {
-      float big_m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
-      float o[2][8] = {{0, 0, 0, 0, 0, 0, 0, 0}, {0, 0, 0, 0, 0, 0, 0, 0}};
-      bool nan_seen[2] = {false, false};
-      const int64_t span = max(u[0].on ? u[0].wl - u[0].wf : 0, u[1].on ? u[1].wl - u[1].wf : 0);
-      for (int64_t d0 = 0; d0 <= span; d0 += 4) {
-        Partial x[2][4];
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            // clamped to a valid partial; only the live ones are folded
-            const int64_t v = u[k].on ? min(u[k].wf + d0 + j, u[k].wl) : 0;
-            const int64_t sl = u[k].on && v < u[k].wsplit ? 1 : 0;
-            const int hh = min(h, GT - 1);
-            x[k][j].ml = coherent_load2(a.part_m + (v * 2 + sl) * (GT * 2) + 2 * hh);
-            const float *src = a.part_o + (v * 2 + sl) * (GT * kHd) + hh * kHd + 8 * r16;
-            x[k][j].o0 = coherent_load4(src);
-            x[k][j].o1 = coherent_load4(src + 4);
+        for (int j = 0; j < 8; ++j) {
+          live[j] = done < count;
+          int64_t sl = own;
+          if (live[j]) {
+            while (rs[jr + 1] == rs[jr]) ++jr;   // empty ranges hold no partial
+            sl = slot_of(jr++);
+            ++done;
           }
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            coherent_wait(x[k][j].ml);
-            coherent_wait(x[k][j].o0);
-            coherent_wait(x[k][j].o1);
+          if (sl == own) {
+            p[j].ml = e.ml[h];
+            p[j].o0 = e.o[h * (kHd / 4) + 2 * r16];
+            p[j].o1 = e.o[h * (kHd / 4) + 2 * r16 + 1];
+          } else {
+            const int ob = (static_cast<int>(sl) * (GT * kHd) + h * kHd + 8 * r16) * 4;
+            const int mb = (static_cast<int>(sl) * GT + h) * 8;
+            if (cross) {
+              p[j].ml = rsrc_load2(rm, mb);
+              p[j].o0 = rsrc_load4(ro, ob);
+              p[j].o1 = rsrc_load4(ro, ob + 16);
+            } else {
+              // past this compute unit's L1 to the XCD's L2
+              p[j].ml = __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rm, mb, 0, 1));
+              p[j].o0 = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, ob, 0, 1));
+              p[j].o1 = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, ob + 16, 0, 1));
+            }
           }
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (u[k].on && h < sp[k]->hcount && u[k].wf + d0 + j <= u[k].wl)
-              fold(x[k][j], big_m[k], l[k], o[k], nan_seen[k]);
-      }
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        if (u[k].on && h < sp[k]->hcount) {
-          const float mul = nan_seen[k] ? nanv : a.v_scale / l[k];
-          const int64_t base_idx = (sp[k]->row0 + h) * kHd + 8 * r16;
-          store4(a, base_idx, make_float4(o[k][0], o[k][1], o[k][2], o[k][3]), mul);
-          store4(a, base_idx + 4, make_float4(o[k][4], o[k][5], o[k][6], o[k][7]), mul);
         }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (live[j]) fold(p[j], big_m, l, o, nan_seen);
       }
+      const float mul = nan_seen ? nanv : a.v_scale / l;
+      const int64_t base_idx = (row0 + h) * kHd + 8 * r16;
+      store4(a, base_idx, make_float4(o[0], o[1], o[2], o[3]), mul);
+      store4(a, base_idx + 4, make_float4(o[4], o[5], o[6], o[7]), mul);
     }
-    if (threadIdx.x == 0) {
-      if (sp0.on) __hip_atomic_store(a.counters + sp0.unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (sp1.on) __hip_atomic_store(a.counters + sp1.unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (lane == 0) __hip_atomic_store(ctr, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   static __device__ void run(const DecodeArgs &a) {
@@ -1123,25 +1366,31 @@ __global__ __launch_bounds__(kFastWaves * 64) void decode_fast_kernel(DecodeArgs
 }
 
 template <typename QS, typename KS, int GT, int BS>
-__global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs a) {
-  Fast<QS, KS, GT, BS, 1>::run_stream(a);
+__global__ __launch_bounds__(512) void decode_pair_kernel(DecodeArgs a) {
+  Fast<QS, KS, GT, BS, 1>::run_pair(a);
 }
 
-// Grid of the balanced split: one single-wave workgroup per SIMD for a
-// 16-bit cache, two for fp8 (fewer if this kernel's occupancy is lower),
-// capped by the workspace capacity the caller sized for.
+// Grid of the balanced split: one 8-wave workgroup (4 streaming waves, one
+// per SIMD, and their 4 helpers) per compute unit.  Dynamic LDS that the
+// kernel does not touch brings a workgroup's LDS above half of the 160 KiB a
+// compute unit has, which keeps a second workgroup off the same unit.
+constexpr int kPairLdsBytes = 84 * 1024;
 template <typename QS, typename KS, int GT, int BS>
 hipError_t launch_stream_gt(const DecodeArgs &a, hipStream_t s) {
-  static const int per_cu = [] {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<QS, KS, GT, BS>, 64, 0) !=
-            hipSuccess || n <= 0)
-      n = 8;
-    return n;
+  static const int fixed = [] {
+    hipFuncAttributes at{};
+    if (hipFuncGetAttributes(&at, reinterpret_cast<const void *>(&decode_pair_kernel<QS, KS, GT, BS>)) !=
+        hipSuccess)
+      return 0;
+    return static_cast<int>(at.sharedSizeBytes);
   }();
-  const int want = std::is_same<KS, FP8S>::value ? kStreamWavesPerCuFp8 : kStreamWavesPerCu16;
-  const int waves = min(a.stream_waves, device_compute_units() * min(per_cu, want));
-  hipLaunchKernelGGL((decode_stream_kernel<QS, KS, GT, BS>), dim3(waves), dim3(64), 0, s, a);
+  const int wgs = min(a.stream_waves / kStreamWavesPerCu, device_compute_units());
+  if (wgs < a.num_xcd) return hipErrorInvalidValue;   // every XCD needs a workgroup
+  // dynamic LDS: the table of range starts (8 bytes per range, plus T) and
+  // range codes (4 bytes per range), at least up to kPairLdsBytes in all
+  const int table = (4 * wgs + 1) * 8 + 4 * wgs * 4;
+  const int dyn = max(table, kPairLdsBytes - fixed);
+  hipLaunchKernelGGL((decode_pair_kernel<QS, KS, GT, BS>), dim3(wgs), dim3(512), dyn, s, a);
   return hipGetLastError();
 }
 

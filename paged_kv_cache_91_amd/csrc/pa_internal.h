@@ -20,7 +20,8 @@ struct DecodeArgs {
   float *part_m;           // split mode: [S][Hq][max_parts]
   float *part_l;           // split mode: [S][Hq][max_parts]
   float *part_o;           // split mode: [S][Hq][max_parts][D]
-  int32_t *counters;       // split mode: arrivals per (sequence, head group); zero between calls
+  int32_t *counters;       // split mode: per (sequence, head group) counters; zero between calls
+  int32_t *ctl;            // balanced split: registration and exit counters; zero between calls
   int64_t num_blocks;
   int32_t num_seqs;
   int32_t num_q_heads;
@@ -35,6 +36,8 @@ struct DecodeArgs {
   int32_t partition_size;  // 0 = single pass
   int32_t stream_waves;    // > 0: balanced (stream-K) split over this many single-wave workgroups
   int32_t max_parts;       // partitions per sequence in the workspace (1 if single pass)
+  int32_t num_xcd;         // balanced split: XCDs of the device (one share each)
+  int32_t share_ranges;    // balanced split: ranges per share the partial slots are sized for
   float scale_log2;        // scale * k_scale * log2(e)
   float v_scale;           // 1 unless fp8
 };
@@ -86,24 +89,30 @@ inline int device_compute_units() {
   return cus;
 }
 
-// Single-wave workgroups per compute unit that the balanced split may
-// launch (its workspace is sized for this many).  A 16-bit cache launches
-// one per SIMD: a second wave on a SIMD only gets the issue slots the first
-// leaves over, falls behind it and finishes its share late.  An fp8 cache
-// carries half the bytes per tile for the same arithmetic, and there two
-// waves per SIMD keep more loads in flight while one of them computes.
-constexpr int kMaxStreamWavesPerCu = 8;
-constexpr int kStreamWavesPerCu16 = 4;
-constexpr int kStreamWavesPerCuFp8 = 8;
+// XCDs of the current device (8, the MI355X count, when it cannot be
+// queried).
+inline int device_xccs() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 8;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || n <= 0) return 8;
+  return n;
+}
+
+// Streaming waves per compute unit in the balanced split (one per SIMD, each
+// with a helper wave); its workspace holds two partials per streaming wave.
+constexpr int kStreamWavesPerCu = 4;
 
 // Workspace layout shared by the API layer and the kernels.
 struct WorkspaceLayout {
   int64_t units;           // S * Hkv * head_groups
   int64_t max_parts;       // fixed partitions per sequence (0 in the balanced split)
-  int64_t stream_waves;    // balanced split: workgroups the partials are sized for
-  int64_t counter_bytes;   // int32 per unit, rounded up to 256 bytes
-  int64_t partial_floats;  // units * max_parts * heads_per_wg * (head_dim + 2)
-  int64_t total_bytes() const { return counter_bytes + partial_floats * 4; }
+  int64_t stream_waves;    // balanced split: streaming waves the workspace is sized for
+  int64_t num_xcd;         // balanced split: shares (one per XCD)
+  int64_t share_ranges;    // balanced split: ranges per share
+  int64_t ctl_bytes;       // balanced split: registration and exit counters, 128-byte lines
+  int64_t counter_bytes;   // per unit: 8 bytes (fixed partitions) or a 128-byte line (balanced split)
+  int64_t partial_floats;  // partials: heads_per_wg * (head_dim + 2) floats each
+  int64_t total_bytes() const { return ctl_bytes + counter_bytes + partial_floats * 4; }
 };
 
 }  // namespace pa_impl

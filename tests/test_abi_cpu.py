@@ -39,20 +39,23 @@ def test_status_strings_and_version():
 
 
 def test_workspace_bytes():
-    # counters: one int32 per (sequence, head group), padded to 256 bytes;
-    # partials: per (sequence, head group, partition, head slot) m, l and D outputs
-    assert pa.pa_decode_workspace_bytes(32, 64, 8, 128, 1024, 32, 512) == 1024 + 32 * 8 * 64 * 8 * 130 * 4
+    # fixed partitions -- counters: 8 bytes per (sequence, head group), padded
+    # to 256 bytes; partials: per (sequence, head group, partition, head slot)
+    # m, l and D outputs
+    assert pa.pa_decode_workspace_bytes(32, 64, 8, 128, 1024, 32, 512) == 2048 + 32 * 8 * 64 * 8 * 130 * 4
     assert pa.pa_decode_workspace_bytes(3, 2, 1, 8, 5, 4, 8) == 256 + 3 * 3 * 2 * 10 * 4
     # group 3 is handled as 4 head slots; group 16 as two head groups of 8
     assert pa.pa_decode_workspace_bytes(2, 12, 4, 64, 4, 16, 32) == 256 + 2 * 4 * 2 * 4 * 66 * 4
-    assert pa.pa_decode_workspace_bytes(100, 32, 2, 64, 1, 16, 16) == 1792 + 100 * 2 * 2 * 1 * 8 * 66 * 4
+    assert pa.pa_decode_workspace_bytes(100, 32, 2, 64, 1, 16, 16) == 3328 + 100 * 2 * 2 * 1 * 8 * 66 * 4
     assert pa.pa_decode_workspace_bytes(3, 2, 1, 8, 5, 4, 0) == 0
     assert pa.pa_decode_workspace_bytes(0, 2, 1, 8, 5, 4, 8) == 0
     assert pa.pa_decode_workspace_bytes(3, 3, 2, 8, 5, 4, 8) == 0      # heads not a multiple
-    # balanced split: two partials per wave, 8 waves per compute unit (256 CUs
-    # assumed when no GPU can be queried, as here)
+    # balanced split: 4 KiB of control words, a 128-byte counter line per
+    # (sequence, head group), and two partial slots per range of each of the
+    # 8 XCD shares, one range per streaming wave: 4 per compute unit (256
+    # compute units and 8 XCDs assumed when no GPU can be queried, as here)
     assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 128, 16, pa.PA_PARTITION_AUTO) == \
-        2048 + 256 * 8 * 2 * 4 * 130 * 4
+        4096 + 512 * 128 + 8 * 128 * 2 * 4 * 130 * 4
     assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 128, 16, -2) == 0
 
 
