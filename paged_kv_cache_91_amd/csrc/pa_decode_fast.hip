@@ -855,7 +855,10 @@ struct Fast {
       while (lds_get(&s_tbl) < 4) __builtin_amdgcn_s_sleep(1);   // the four helpers have filled it
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
-    helper_main(a, bx, T, x, x * (a.share_ranges) + 4 * reg + slot, lane, s_exit, rs, rc);
+    int64_t lo = 0, hi = 0;
+    if (reg < wgs_on(x, NX)) range_of(sh, 4 * reg + slot, lo, hi);
+    helper_main(a, bx, T, x, x * (a.share_ranges) + 4 * reg + slot, lo, hi, lane, n_lane, cnt0, incl0, s_exit,
+                rs, rc);
   }
 
   // The streamer's tile range [lo, hi) of the T-tile list.  Finished
@@ -1034,8 +1037,9 @@ struct Fast {
   // + range): first the rows of empty (zero) and out-of-range (NaN)
   // sequences, then the mailbox until the streamer is done, then the exit
   // count.
-  static __device__ void helper_main(const DecodeArgs &a, Box &bx, int64_t T, int64_t x, int64_t rid, int lane,
-                                     int &s_exit, const int64_t *rs, const int *rc) {
+  static __device__ void helper_main(const DecodeArgs &a, Box &bx, int64_t T, int64_t x, int64_t rid, int64_t lo,
+                                     int64_t hi, int lane, int n_lane, int64_t cnt0, int64_t incl0, int &s_exit,
+                                     const int64_t *rs, const int *rc) {
     const int NX = a.num_xcd;
     const int64_t nh = 4 * static_cast<int64_t>(gridDim.x);
     const int maxn = a.max_blocks * BS;
@@ -1050,13 +1054,40 @@ struct Fast {
                make_float4(fill, fill, fill, fill), 1.0f);
     }
 
+    Pre pre;
+    pre.on = false;
+    if (lo < hi) {
+      const Cursor c = locate(a, hi - 1, lane, n_lane, cnt0, incl0);
+      const int64_t gu = c.G + static_cast<int64_t>(c.u) * c.nts, glast = gu + c.nts - 1;
+      if (gu < lo || glast >= hi) {
+        int64_t r1, count, rl;
+        holders(T, gu, glast, rs, rc, r1, count, rl);
+        if (count <= kPre) {
+          pre.on = true;
+          pre.unit = static_cast<int64_t>(c.s) * (a.num_kv_heads * a.head_groups) + c.u;
+          pre.count = count;
+          pre.cross = (rc[r1] >> 20) != (rc[rl] >> 20);
+          int64_t jr = r1;
+#pragma unroll
+          for (int j = 0; j < kPre; ++j) {
+            pre.slot[j] = -1;
+            if (j < count) {
+              while (rs[jr + 1] == rs[jr]) ++jr;
+              pre.slot[j] = ((rc[jr] >> 20) * a.share_ranges + (rc[jr] & 0xfffff)) * 2 + (rs[jr] < gu ? 1 : 0);
+              ++jr;
+            }
+          }
+        }
+      }
+    }
+
     int tail = 0;
     for (;;) {
       const int done = lds_get(&bx.done);
       const int head = lds_get(&bx.head);
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       if (tail < head) {
-        handle(a, T, rid, bx.m[tail % kMail], lane, rs, rc);
+        handle(a, T, rid, bx.m[tail % kMail], lane, rs, rc, pre);
         ++tail;
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         if (lane == 0) lds_put(&bx.tail, tail);
@@ -1098,6 +1129,36 @@ struct Fast {
     }
   }
 
+  // The ranges holding the unit's tiles [gu, glast]: the first (r1) and
+  // last (rl) of them and how many are non-empty (count).  The range holding
+  // gu is found from a proportional guess (ranges are near-equal, so it is a
+  // step or two away).
+  static __device__ __forceinline__ void holders(int64_t T, int64_t gu, int64_t glast, const int64_t *rs,
+                                                 const int *rc, int64_t &r1, int64_t &count, int64_t &rl) {
+    const int64_t NR = 4 * static_cast<int64_t>(gridDim.x);
+    r1 = min(NR - 1, static_cast<int64_t>(static_cast<float>(gu) * static_cast<float>(NR) / static_cast<float>(T)));
+    while (rs[r1] > gu) --r1;
+    while (rs[r1 + 1] <= gu) ++r1;
+    count = 1;
+    rl = r1;
+    for (int64_t j = r1 + 1; j < NR && rs[j] <= glast; ++j)
+      if (rs[j + 1] > rs[j]) {
+        ++count;
+        rl = j;
+      }
+  }
+
+  // The unit a range ends inside, when the range cuts it, worked out while
+  // the range streams: its holder count and partial slots (tile order), so
+  // that the merge at the range's end, the one on the kernel's critical
+  // path, needs no table walk and issues all its loads at once.
+  static constexpr int kPre = 8;
+  struct Pre {
+    bool on, cross;
+    int64_t unit, count;
+    int64_t slot[kPre];
+  };
+
   // The helper's work for one mailbox entry of the streamer with range index
   // `rid`.  A whole unit: its output rows.  A split unit: the range's partial
   // is published (partial slot (range index, side); side 1 when the range
@@ -1106,7 +1167,7 @@ struct Fast {
   // in tile order (this one straight from LDS), writes the rows and resets
   // the counter to zero.
   static __device__ void handle(const DecodeArgs &a, int64_t T, int64_t rid, const Mail &e, int lane,
-                                const int64_t *rs, const int *rc) {
+                                const int64_t *rs, const int *rc, Pre &pre) {
     const int NX = a.num_xcd;
     const int hc = e.hcount;
     const int64_t row0 = e.row0;
@@ -1120,20 +1181,16 @@ struct Fast {
     }
     const int64_t gu = e.gu, glast = e.gu + e.nts - 1;
     const int64_t sr = a.share_ranges;
-    const int64_t NR = 4 * static_cast<int64_t>(gridDim.x);
-    // the range holding gu (ranges are near-equal, so the proportional guess
-    // is a step or two away), then the non-empty ranges up to glast
-    int64_t r1 = min(NR - 1, static_cast<int64_t>(static_cast<float>(gu) * static_cast<float>(NR) /
-                                                  static_cast<float>(T)));
-    while (rs[r1] > gu) --r1;
-    while (rs[r1 + 1] <= gu) ++r1;
-    int64_t count = 1, rl = r1;
-    for (int64_t j = r1 + 1; j < NR && rs[j] <= glast; ++j)
-      if (rs[j + 1] > rs[j]) {
-        ++count;
-        rl = j;
-      }
-    const bool cross = (rc[r1] >> 20) != (rc[rl] >> 20);
+    const bool known = pre.on && e.unit == pre.unit;   // the range's last unit, worked out ahead
+    int64_t r1 = 0, count, rl = 0;
+    bool cross;
+    if (known) {
+      count = pre.count;
+      cross = pre.cross;
+    } else {
+      holders(T, gu, glast, rs, rc, r1, count, rl);
+      cross = (rc[r1] >> 20) != (rc[rl] >> 20);
+    }
     // partial slot of range j for this unit
     auto slot_of = [&](int64_t j) {
       return ((rc[j] >> 20) * sr + (rc[j] & 0xfffff)) * 2 + (rs[j] < gu ? 1 : 0);
@@ -1174,8 +1231,12 @@ struct Fast {
           live[j] = done < count;
           int64_t sl = own;
           if (live[j]) {
-            while (rs[jr + 1] == rs[jr]) ++jr;   // empty ranges hold no partial
-            sl = slot_of(jr++);
+            if (known) {
+              sl = pre.slot[j];              // count <= kPre == 8: one batch
+            } else {
+              while (rs[jr + 1] == rs[jr]) ++jr;   // empty ranges hold no partial
+              sl = slot_of(jr++);
+            }
             ++done;
           }
           if (sl == own) {
