@@ -177,13 +177,18 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *                 merged in increasing p, so the output does not depend on
  *                 the order in which partitions finish.
  *   workspace     device scratch of at least pa_decode_workspace_bytes(...)
- *                 bytes when partition_size > 0 (else may be NULL).  Its
- *                 leading bytes hold the arrival counters, which MUST be zero
- *                 before the first call that uses the workspace: zero-fill
- *                 the whole workspace once when it is allocated.  Every call
- *                 leaves the counters zero again; the rest may hold
- *                 anything.  Calls that may run concurrently must not share
- *                 one workspace.
+ *                 bytes when partition_size != 0 (else may be NULL).  Its
+ *                 leading bytes hold counters, which MUST be zero before the
+ *                 first call that uses the workspace: zero-fill the whole
+ *                 workspace once when it is allocated.  Every call leaves
+ *                 the counters zero again; the rest may hold anything.  Calls
+ *                 that may run concurrently must not share one workspace,
+ *                 and a workspace serves one partition mode (zero-fill it
+ *                 again before switching).  The balanced split relies on
+ *                 the dispatcher dealing workgroups to the XCDs in turn; a
+ *                 launch that finds otherwise writes NaN rows and marks the
+ *                 workspace, and every later call with a marked workspace
+ *                 writes NaN rows until it is zero-filled again.
  */
 int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
               const pa_kv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,

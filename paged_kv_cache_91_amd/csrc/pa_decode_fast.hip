@@ -666,10 +666,15 @@ struct Fast {
   // one per boundary) uses device-coherent stores and loads.  The counters
   // are device-scope atomics either way.
   //
-  // Check.  The grid's last helper compares every XCD's registration count
-  // with n(x); if the dispatcher placed the workgroups otherwise, some
-  // ranges were not streamed, and it turns every output row into NaN
-  // rather than leave rows unwritten.  It then resets the counters.
+  // Check.  If the dispatcher placed the workgroups otherwise, some XCD
+  // gets more than n(x) of them, and a workgroup that draws an index >= n(x)
+  // knows it at once: it marks the workspace (a poison word) and writes NaN
+  // into every output row, so rows of ranges nobody streamed are NaN rather
+  // than stale.  A marked workspace makes every later call write NaN rows
+  // (its counters can no longer be trusted) until it is zero-filled again.
+  // When every XCD's last index n(x) - 1 has been drawn, the registrations
+  // are complete and exact; the last of those workgroups resets the
+  // registration counters, early in the launch and off its critical path.
   // -------------------------------------------------------------------------
 
   // workgroups the dispatcher places on XCD x, and share x's tiles and ranges
@@ -772,13 +777,20 @@ struct Fast {
     return c;
   }
 
-  // Workspace control words, one 128-byte line each: the count of finished
-  // workgroup groups at ctl[0], XCD x's registration count at
-  // ctl[32 * (1 + x)] (x < 16), workgroup group g's count of finished
-  // workgroups at ctl[32 * (17 + g)] (g < 8); the unit counters at
-  // a.counters + 32 * unit (one 128-byte line each, 64-bit).
+  // Workspace control words, one 128-byte line each: the count of XCDs
+  // whose registrations are complete at ctl[0], XCD x's registration count
+  // at ctl[32 * (1 + x)] (x < 16), the poison word at ctl[32 * 17]; the unit
+  // counters at a.counters + 32 * unit (one 128-byte line each, 64-bit).
   static __device__ __forceinline__ int *reg_ctr(const DecodeArgs &a, int64_t x) { return a.ctl + 32 * (x + 1); }
-  static __device__ __forceinline__ int *group_ctr(const DecodeArgs &a, int64_t g) { return a.ctl + 32 * (17 + g); }
+  static __device__ __forceinline__ int *poison_word(const DecodeArgs &a) { return a.ctl + 32 * 17; }
+
+  // NaN into output rows first, first + step, ... of the batch
+  static __device__ void nan_rows(const DecodeArgs &a, int64_t first, int64_t step, int lane) {
+    const float nanv = __builtin_nanf("");
+    const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;
+    for (int64_t r = first; r < rows; r += step)
+      for (int i = lane; i < kHd / 4; i += 64) store4(a, r * kHd + 4 * i, make_float4(nanv, nanv, nanv, nanv), 1.0f);
+  }
   static __device__ __forceinline__ uint64_t *unit_ctr(const DecodeArgs &a, int64_t unit) {
     return reinterpret_cast<uint64_t *>(a.counters) + 16 * unit;
   }
@@ -786,7 +798,7 @@ struct Fast {
   static __device__ void run_pair(const DecodeArgs &a) {
     __shared__ Box box[4];
     __shared__ uint4 s_q[4][kQSlots][GT * 16];
-    __shared__ int s_reg, s_exit, s_tbl;
+    __shared__ int s_reg, s_poison, s_tbl;
     // dynamic LDS: the table of range starts (the helpers' lookups)
     extern __shared__ int64_t pa_dyn_lds[];
     const int wave = uniform(static_cast<int>(threadIdx.x >> 6));
@@ -798,9 +810,19 @@ struct Fast {
     // partials relies on all its waves sharing one L2)
     const int NX = a.num_xcd;
     const int64_t x = static_cast<int64_t>(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15) % NX;
-    if (threadIdx.x == 0) {
-      s_reg = __hip_atomic_fetch_add(reg_ctr(a, x), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_exit = 0;
+    // the first helper registers and reads the poison word while every wave
+    // loads the lengths (the two waits overlap)
+    int reg_got = 0, poison_got = 0;
+    if (threadIdx.x == 256) {
+      reg_got = __hip_atomic_fetch_add(reg_ctr(a, x), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      poison_got = __hip_atomic_load(poison_word(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    int n_lane;
+    int64_t cnt0, incl0;
+    const int64_t T = count_tiles(a, lane, n_lane, cnt0, incl0);
+    if (threadIdx.x == 256) {
+      s_reg = reg_got;
+      s_poison = poison_got;
       s_tbl = 0;
     }
     if (lane == 0) {
@@ -813,17 +835,38 @@ struct Fast {
     }
     __syncthreads();
     const int64_t reg = s_reg;
-
-    int n_lane;
-    int64_t cnt0, incl0;
-    const int64_t T = count_tiles(a, lane, n_lane, cnt0, incl0);
+    const int64_t n_x = wgs_on(x, NX);
+    if (reg >= n_x || s_poison != 0) {
+      // a misplaced grid (this workgroup is surplus on its XCD) or a marked
+      // workspace: NaN rows (all of them from the surplus workgroup, a
+      // strided share from each workgroup of a marked one), nothing else
+      if (helper) {
+        if (reg >= n_x && wave == 4 && lane == 0)
+          __hip_atomic_store(poison_word(a), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (reg >= n_x)
+          nan_rows(a, wave - 4, 4, lane);
+        else
+          nan_rows(a, (wave - 4) * static_cast<int64_t>(gridDim.x) + blockIdx.x, 4 * static_cast<int64_t>(gridDim.x),
+                   lane);
+      }
+      return;
+    }
+    if (wave == 4 && reg == n_x - 1) {
+      // the last registration on this XCD; the last XCD to complete resets
+      // the counters (every workgroup of the grid has registered by then)
+      const int xcds = min(NX, static_cast<int>(gridDim.x));
+      int done = 0;
+      if (lane == 0) done = __hip_atomic_fetch_add(a.ctl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (uniform(done) == xcds - 1) {
+        if (lane < NX) __hip_atomic_store(reg_ctr(a, lane), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) __hip_atomic_store(a.ctl, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
     const Share sh = share_geom(T, NX, x);
     if (!helper) {
-      if (reg < wgs_on(x, NX)) {
-        int64_t lo, hi;
-        range_of(sh, 4 * reg + slot, lo, hi);
-        if (lo < hi) stream(a, bx, s_q[slot], lo, hi, lane, n_lane, cnt0, incl0);
-      }
+      int64_t lo, hi;
+      range_of(sh, 4 * reg + slot, lo, hi);
+      if (lo < hi) stream(a, bx, s_q[slot], lo, hi, lane, n_lane, cnt0, incl0);
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       if (lane == 0) lds_put(&bx.done, 1);
       return;
@@ -855,10 +898,9 @@ struct Fast {
       while (lds_get(&s_tbl) < 4) __builtin_amdgcn_s_sleep(1);   // the four helpers have filled it
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
-    int64_t lo = 0, hi = 0;
-    if (reg < wgs_on(x, NX)) range_of(sh, 4 * reg + slot, lo, hi);
-    helper_main(a, bx, T, x, x * (a.share_ranges) + 4 * reg + slot, lo, hi, lane, n_lane, cnt0, incl0, s_exit,
-                rs, rc);
+    int64_t lo, hi;
+    range_of(sh, 4 * reg + slot, lo, hi);
+    helper_main(a, bx, T, x * (a.share_ranges) + 4 * reg + slot, lo, hi, lane, n_lane, cnt0, incl0, rs, rc);
   }
 
   // The streamer's tile range [lo, hi) of the T-tile list.  Finished
@@ -1035,12 +1077,10 @@ struct Fast {
 
   // The helper of the streamer with range index `rid` (share * share_ranges
   // + range): first the rows of empty (zero) and out-of-range (NaN)
-  // sequences, then the mailbox until the streamer is done, then the exit
-  // count.
-  static __device__ void helper_main(const DecodeArgs &a, Box &bx, int64_t T, int64_t x, int64_t rid, int64_t lo,
-                                     int64_t hi, int lane, int n_lane, int64_t cnt0, int64_t incl0, int &s_exit,
-                                     const int64_t *rs, const int *rc) {
-    const int NX = a.num_xcd;
+  // sequences, then the mailbox until the streamer is done.
+  static __device__ void helper_main(const DecodeArgs &a, Box &bx, int64_t T, int64_t rid, int64_t lo, int64_t hi,
+                                     int lane, int n_lane, int64_t cnt0, int64_t incl0, const int64_t *rs,
+                                     const int *rc) {
     const int64_t nh = 4 * static_cast<int64_t>(gridDim.x);
     const int maxn = a.max_blocks * BS;
     const int hid = static_cast<int>(threadIdx.x >> 6) - 4;
@@ -1095,37 +1135,6 @@ struct Fast {
       }
       if (done) break;
       __builtin_amdgcn_s_sleep(1);
-    }
-
-    // The grid's last helper checks the registrations and resets the
-    // counters.  It is found in three steps, so that no counter takes more
-    // than a few dozen atomics: the workgroup's last helper (LDS), the last
-    // workgroup of its group (workgroups b with b % 8 == g), the last group.
-    __builtin_amdgcn_s_waitcnt(0x0f70);        // vmcnt(0): this helper's stores have landed
-    int last = 0;
-    if (lane == 0) last = __hip_atomic_fetch_add(&s_exit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 3;
-    if (!uniform(last)) return;
-    const int g = blockIdx.x & 7;
-    const int in_group = (static_cast<int>(gridDim.x) - g + 7) >> 3;
-    const int groups = min(8, static_cast<int>(gridDim.x));
-    if (lane == 0)
-      last = __hip_atomic_fetch_add(group_ctr(a, g), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == in_group - 1;
-    if (!uniform(last)) return;
-    if (lane == 0) last = __hip_atomic_fetch_add(a.ctl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == groups - 1;
-    if (!uniform(last)) return;
-    bool missing = false;
-    if (lane < NX) {
-      missing = __hip_atomic_load(reg_ctr(a, lane), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
-                wgs_on(lane, NX);
-      __hip_atomic_store(reg_ctr(a, lane), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (lane < 8) __hip_atomic_store(group_ctr(a, lane), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (lane == 0) __hip_atomic_store(a.ctl, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (__builtin_amdgcn_ballot_w64(missing) != 0) {
-      const float nanv = __builtin_nanf("");
-      const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;
-      for (int64_t i = lane; i < rows * (kHd / 4); i += 64)
-        store4(a, 4 * i, make_float4(nanv, nanv, nanv, nanv), 1.0f);
     }
   }
 

@@ -21,7 +21,7 @@ struct DecodeArgs {
   float *part_l;           // split mode: [S][Hq][max_parts]
   float *part_o;           // split mode: [S][Hq][max_parts][D]
   int32_t *counters;       // split mode: per (sequence, head group) counters; zero between calls
-  int32_t *ctl;            // balanced split: registration and exit counters; zero between calls
+  int32_t *ctl;            // balanced split: registration counters and the poison word; zero between calls
   int64_t num_blocks;
   int32_t num_seqs;
   int32_t num_q_heads;
@@ -109,7 +109,7 @@ struct WorkspaceLayout {
   int64_t stream_waves;    // balanced split: streaming waves the workspace is sized for
   int64_t num_xcd;         // balanced split: shares (one per XCD)
   int64_t share_ranges;    // balanced split: ranges per share
-  int64_t ctl_bytes;       // balanced split: registration and exit counters, 128-byte lines
+  int64_t ctl_bytes;       // balanced split: registration counters and the poison word, 128-byte lines
   int64_t counter_bytes;   // per unit: 8 bytes (fixed partitions) or a 128-byte line (balanced split)
   int64_t partial_floats;  // partials: heads_per_wg * (head_dim + 2) floats each
   int64_t total_bytes() const { return ctl_bytes + counter_bytes + partial_floats * 4; }

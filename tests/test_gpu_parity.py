@@ -340,3 +340,52 @@ def test_nondefault_stream():
                            stream=s)
     s.synchronize()
     assert max_err(out_f64(out), ref) <= 2e-2
+
+
+# ---------------------------------------------------------------------------
+# the balanced split's placement check, forced from the host through the
+# workspace's control words (int32 index 32 * (1 + x): XCD x's registration
+# count; 32 * 17: the poison word)
+# ---------------------------------------------------------------------------
+
+def _auto_ws(wl):
+    return pa.new_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                            wl.max_blocks_per_seq, wl.block_size, pa.PA_PARTITION_AUTO, device=DEV)
+
+
+def _auto(dev, ws):
+    out = torch.full_like(dev.q, float("nan"))
+    return out_f64(pa.pa_decode(dev.q, dev.pool, dev.tables, dev.ctx, dev.wl.scale, out=out,
+                                partition_size=pa.PA_PARTITION_AUTO, workspace=ws,
+                                q_dtype=dev.wl.q_dtype))
+
+
+@pytest.mark.parametrize("surplus", ["one_xcd", "every_xcd", "poison_word"])
+def test_placement_check_marks_workspace_until_zeroed(surplus):
+    """A workgroup that draws an index past its XCD's share (as it would if
+    the dispatcher did not deal workgroups to the XCDs in turn) writes NaN
+    rows and marks the workspace; a marked workspace gives NaN rows until it
+    is zero-filled, and then the results are exact again."""
+    wl = W.config2(seed=44, num_seqs=6, ctx_range=(10, 500), num_blocks=256)
+    dev = DeviceWorkload(wl)
+    ref = oracle_out(wl)
+    ws = _auto_ws(wl)
+    assert max_err(_auto(dev, ws), ref) <= 2e-2
+    words = ws.view(torch.int32)
+    if surplus == "one_xcd":
+        words[32 * 1] = 1 << 20
+    elif surplus == "every_xcd":
+        for x in range(16):
+            words[32 * (1 + x)] = 1 << 20
+    else:
+        words[32 * 17] = 1
+    got = _auto(dev, ws)
+    if surplus == "one_xcd":
+        assert np.isnan(got).any()
+    else:
+        assert np.isnan(got).all()
+    assert int(words[32 * 17].item()) == 1
+    assert np.isnan(_auto(dev, ws)).all()           # marked: every row NaN
+    ws.zero_()
+    for _ in range(2):
+        assert max_err(_auto(dev, ws), ref) <= 2e-2
