@@ -115,7 +115,7 @@ bool workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_head
     w->share_ranges = pa_impl::kStreamWavesPerCu * ceil_div(w->stream_waves / pa_impl::kStreamWavesPerCu, w->num_xcd);
     w->ctl_bytes = 4096;
     w->counter_bytes = w->units * 128;
-    w->partial_floats = w->num_xcd * w->share_ranges * 2 * hpw * (static_cast<int64_t>(head_dim) + 2);
+    w->partial_floats = w->num_xcd * w->share_ranges * 2 * (hpw * static_cast<int64_t>(head_dim) + pa_impl::kSlotMlFloats);
   } else {
     w->max_parts = ceil_div(static_cast<int64_t>(max_blocks_per_seq) * block_size, partition_size);
     w->counter_bytes = ceil_div(w->units * 8, 256) * 256;
@@ -270,7 +270,7 @@ int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
     float *ws = reinterpret_cast<float *>(base + w.ctl_bytes + w.counter_bytes);
     const int64_t slots = w.num_xcd * w.share_ranges * 2;
     a.part_o = ws;                                     // [share][range][side][head][D]
-    a.part_m = ws + slots * hpw * pool->head_dim;      // [share][range][side][head][m, l]
+    a.part_m = ws + slots * hpw * pool->head_dim;      // [share][range][side][32]: (m, l) per head
   } else if (partition_size > 0) {
     pa_impl::WorkspaceLayout w{};
     workspace_layout(num_seqs, num_q_heads, pool->num_kv_heads, pool->head_dim, max_blocks_per_seq,

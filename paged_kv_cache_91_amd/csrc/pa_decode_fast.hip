@@ -660,11 +660,14 @@ struct Fast {
   //
   // Exchange.  The partials of a unit inside one share are written and
   // merged by waves of one XCD, so they go through that XCD's L2 with
-  // ordinary stores and loads that only skip the compute unit's L1 (a
-  // device-coherent store is written through to memory and slows every
-  // wave's K/V loads down).  A unit that crosses a share boundary (at most
-  // one per boundary) uses device-coherent stores and loads.  The counters
-  // are device-scope atomics either way.
+  // ordinary stores and loads (a device-coherent store is written through
+  // to memory and slows every wave's K/V loads down; a device-scope acquire
+  // would drop the XCD's L2 lines the merge is about to read).  The loads
+  // may hit the merging compute unit's L1, which is safe because a slot's
+  // lines are loaded only after the slot is counted in, once per launch,
+  // and no two slots share a line.  A unit that crosses a share boundary
+  // (at most one per boundary) uses device-coherent stores and loads.  The
+  // counters are device-scope atomics either way.
   //
   // Check.  If the dispatcher placed the workgroups otherwise, some XCD
   // gets more than n(x) of them, and a workgroup that draws an index >= n(x)
@@ -1205,17 +1208,18 @@ struct Fast {
       return ((rc[j] >> 20) * sr + (rc[j] & 0xfffff)) * 2 + (rs[j] < gu ? 1 : 0);
     };
     const auto ro = float_rsrc(a.part_o, NX * sr * 2 * GT * kHd);
-    const auto rm = float_rsrc(a.part_m, NX * sr * 2 * GT * 2);
+    const auto rm = float_rsrc(a.part_m, NX * sr * 2 * kSlotMlFloats);
     const int own = static_cast<int>(rid * 2 + e.side);
     if (cross) {
       for (int i = lane; i < GT * (kHd / 4); i += 64) rsrc_store4(ro, (own * (GT * kHd) + 4 * i) * 4, e.o[i]);
-      if (lane < GT) rsrc_store2(rm, (own * GT + lane) * 8, e.ml[lane]);
+      if (lane < GT) rsrc_store2(rm, (own * kSlotMlFloats + 2 * lane) * 4, e.ml[lane]);
     } else {
       typedef uint32_t w4 __attribute__((ext_vector_type(4)));
       typedef uint32_t w2 __attribute__((ext_vector_type(2)));
       for (int i = lane; i < GT * (kHd / 4); i += 64)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(w4, e.o[i]), ro, (own * (GT * kHd) + 4 * i) * 4, 0, 0);
-      if (lane < GT) __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(w2, e.ml[lane]), rm, (own * GT + lane) * 8, 0, 0);
+      if (lane < GT)
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(w2, e.ml[lane]), rm, (own * kSlotMlFloats + 2 * lane) * 4, 0, 0);
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);        // vmcnt(0): published before counted
     uint64_t *ctr = unit_ctr(a, e.unit);
@@ -1254,13 +1258,15 @@ struct Fast {
             p[j].o1 = e.o[h * (kHd / 4) + 2 * r16 + 1];
           } else {
             const int ob = (static_cast<int>(sl) * (GT * kHd) + h * kHd + 8 * r16) * 4;
-            const int mb = (static_cast<int>(sl) * GT + h) * 8;
+            const int mb = (static_cast<int>(sl) * kSlotMlFloats + 2 * h) * 4;
             if (cross) {
               p[j].ml = rsrc_load2(rm, mb);
               p[j].o0 = rsrc_load4(ro, ob);
               p[j].o1 = rsrc_load4(ro, ob + 16);
             } else {
-              // past this compute unit's L1 to the XCD's L2
+              // from the XCD's L2: no line of a slot is loaded before the
+              // slot is counted in, and no two slots share a line, so this
+              // compute unit's L1 holds no stale copy
               p[j].ml = __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rm, mb, 0, 1));
               p[j].o0 = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, ob, 0, 1));
               p[j].o1 = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, ob + 16, 0, 1));

@@ -101,6 +101,11 @@ inline int device_xccs() {
 // Streaming waves per compute unit in the balanced split (one per SIMD, each
 // with a helper wave); its workspace holds two partials per streaming wave.
 constexpr int kStreamWavesPerCu = 4;
+// Balanced split: floats per partial slot's (m, l) block, one 128-byte line
+// (pairs for up to 16 heads).  No two slots share a line, so a compute unit
+// that loads one slot never caches a line of another slot that is not yet
+// published.
+constexpr int kSlotMlFloats = 32;
 
 // Workspace layout shared by the API layer and the kernels.
 struct WorkspaceLayout {

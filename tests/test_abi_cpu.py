@@ -53,9 +53,10 @@ def test_workspace_bytes():
     # balanced split: 4 KiB of control words, a 128-byte counter line per
     # (sequence, head group), and two partial slots per range of each of the
     # 8 XCD shares, one range per streaming wave: 4 per compute unit (256
-    # compute units and 8 XCDs assumed when no GPU can be queried, as here)
+    # compute units and 8 XCDs assumed when no GPU can be queried, as here);
+    # a slot holds D outputs per head and a 128-byte line of (m, l) pairs
     assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 128, 16, pa.PA_PARTITION_AUTO) == \
-        4096 + 512 * 128 + 8 * 128 * 2 * 4 * 130 * 4
+        4096 + 512 * 128 + 8 * 128 * 2 * (4 * 128 + 32) * 4
     assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 128, 16, -2) == 0
 
 
