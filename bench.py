@@ -56,6 +56,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=64,
                     help="sequences of the batch the oracle baseline processes")
+    ap.add_argument("--workload", default="llama3-8b",
+                    choices=["llama3-8b", "mha-13b", "prefix-cow", "fp8-long"],
+                    help="llama3-8b: the step above (default).  The others time pa_decode alone on the "
+                         "13B-shaped fp16 batch, the prefix-sharing batch or the long-context fp8 batch "
+                         "(one JSON line per partition setting)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run pa_copy_blocks over MIB MiB of blocks (counter calibration) and exit")
     return ap.parse_args()
@@ -109,6 +114,8 @@ def main():
 
     if args.calibrate_copy:
         return calibrate_copy(args.calibrate_copy, pa, torch, dev)
+    if args.workload != "llama3-8b":
+        return other_workload(args, pa, W, torch, dev)
 
     t0 = time.time()
     wl = W.config2()
@@ -270,6 +277,83 @@ def cpu_baseline(wl, new_k, new_v, nseq, min_seconds=10.0, max_passes=50):
                       f"(one step each: write + decode, float64 numpy), {total:.1f}s in total",
             "seconds_per_step": round(dt, 4), "host_cpus": cores, "cpu_model": cpu_model,
             "decode_tokens_per_s_per_layer": round(len(idx) / dt, 3)}
+
+
+def other_workload(args, pa, W, torch, dev):
+    """pa_decode alone on one of the other batches, timed with HIP events per
+    call (after its cache write or block copies, which are not timed).  Their
+    pools are 1-21 GB, past the 256 MB last-level cache, except the prefix
+    batch's (about 40 MB of distinct blocks): its numbers are cache-warm."""
+    import numpy as np
+    t0 = time.time()
+    wl = {"mha-13b": W.config3, "prefix-cow": W.config4, "fp8-long": W.config5}[args.workload]()
+    log(f"[bench] {args.workload} generated in {time.time() - t0:.1f}s: S={wl.num_seqs} "
+        f"kv_bytes={wl.kv_bytes() / 1e9:.3f} GB")
+    storage = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "fp8_e4m3": torch.uint8}
+
+    def to_dev(a, dtype):
+        a = np.ascontiguousarray(a)
+        if dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    # pools: only the blocks some table (or copy pair) names carry data
+    tables = wl.block_tables if wl.tables_before_copy is None else wl.tables_before_copy
+    kp = torch.zeros(wl.k_pool.shape, dtype=storage[wl.kv_dtype], device=dev)
+    vp = torch.zeros_like(kp)
+    if wl.write_k is None:
+        ids = np.unique(np.concatenate([tables[s, :-(-int(n) // wl.block_size)]
+                                        for s, n in enumerate(wl.context_lens)]).astype(np.int64))
+        if wl.copy_pairs is not None:
+            ids = np.union1d(ids, wl.copy_pairs.ravel())
+        it = torch.from_numpy(ids).to(dev)
+        kp[it] = to_dev(wl.k_pool[ids], wl.kv_dtype)
+        vp[it] = to_dev(wl.v_pool[ids], wl.kv_dtype)
+    pool = pa.make_pool(kp, vp, dtype=wl.kv_dtype, k_scale=wl.k_scale, v_scale=wl.v_scale)
+    if wl.write_k is not None:
+        pa.pa_write_kv(to_dev(wl.write_k, wl.write_src_dtype), to_dev(wl.write_v, wl.write_src_dtype),
+                       torch.from_numpy(wl.slot_mapping.astype(np.int64)).to(dev), pool,
+                       src_dtype=wl.write_src_dtype)
+    tb = torch.from_numpy(np.ascontiguousarray(tables, dtype=np.int32)).to(dev)
+    if wl.copy_pairs is not None:
+        pa.pa_copy_blocks(pool, torch.from_numpy(wl.copy_pairs.astype(np.int64)).to(dev))
+        tb = torch.from_numpy(np.ascontiguousarray(wl.block_tables, dtype=np.int32)).to(dev)
+    q = to_dev(wl.q, wl.q_dtype)
+    ctx = torch.from_numpy(wl.context_lens.astype(np.int32)).to(dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    kv_bytes = wl.kv_bytes()
+    parts = [-1, 0] + ([wl.partition_size] if wl.partition_size > 0 else [256])
+    for part in parts:
+        ws = pa.new_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                              wl.max_blocks_per_seq, wl.block_size, part, device=dev) if part else None
+        for _ in range(max(args.warmup, 3)):
+            pa.pa_decode(q, pool, tb, ctx, wl.scale, out=out, partition_size=part, workspace=ws,
+                         q_dtype=wl.q_dtype, stream=stream)
+        steps = max(1, min(args.steps, 50))
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record(stream)
+            pa.pa_decode(q, pool, tb, ctx, wl.scale, out=out, partition_size=part, workspace=ws,
+                         q_dtype=wl.q_dtype, stream=stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+        med = us[len(us) // 2]
+        gbs = kv_bytes / (med * 1e-6) / 1e9
+        assert bool(torch.isfinite(out.float()).all()), "non-finite output"
+        print(json.dumps({
+            "workload": args.workload, "partition_size": part, "kv_bytes": kv_bytes,
+            "kv_dtype": wl.kv_dtype, "num_seqs": wl.num_seqs, "num_q_heads": wl.num_q_heads,
+            "num_kv_heads": wl.num_kv_heads, "block_size": wl.block_size,
+            "decode_us": {"median": round(med, 2), "p10": round(us[len(us) // 10], 2),
+                          "p90": round(us[(9 * len(us)) // 10], 2), "calls": steps},
+            "kv_gbs": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "decode_tokens_per_s_per_layer": round(wl.num_seqs / (med * 1e-6), 1),
+            "cache": "warm (fits the last-level cache)" if kv_bytes < (256 << 20) else "pools exceed the last-level cache",
+        }), flush=True)
 
 
 def calibrate_copy(mib, pa, torch, dev):
