@@ -1402,29 +1402,29 @@ struct Fast {
     if (!s_last) return;
 
     // merge every partition of this (sequence, head group) in partition
-    // order, four partitions' loads in flight at a time
+    // order, eight partitions' loads in flight at a time
     const float *bo = a.part_o + unit * a.max_parts * (GT * kHd);
     const float *bml = a.part_m + unit * a.max_parts * (GT * 2);
     for (int i = tid; i < hcount * (kHd / 4); i += kThreads) {
       const int h = i >> 5, d4 = i & 31;
       float big_m = -INFINITY, l = 0.0f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       bool nan_seen = false;
-      for (int p0 = 0; p0 < nparts; p0 += 4) {
-        Partial x[4];
+      for (int p0 = 0; p0 < nparts; p0 += 8) {
+        Partial x[8];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < 8; ++k) {
           const int pp = min(p0 + k, nparts - 1);
           x[k].ml = coherent_load2(bml + pp * GT * 2 + 2 * h);
           x[k].o0 = coherent_load4(bo + pp * GT * kHd + h * kHd + 4 * d4);
           x[k].o1 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < 8; ++k) {
           coherent_wait(x[k].ml);
           coherent_wait(x[k].o0);
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int k = 0; k < 8; ++k)
           if (p0 + k < nparts) fold(x[k], big_m, l, o, nan_seen);
       }
       store4(a, (row0 + h) * kHd + 4 * d4, make_float4(o[0], o[1], o[2], o[3]),
@@ -1434,11 +1434,15 @@ struct Fast {
   }
 };
 
+// Waves per workgroup of the fixed-partition kernel: four share a whole
+// context (single pass); one takes a whole partition (split), so that the
+// per-workgroup set-up and publish are spread over all of its tiles.
 constexpr int kFastWaves = 4;
+constexpr int kSplitWaves = 1;
 
-template <typename QS, typename KS, int GT, int BS>
-__global__ __launch_bounds__(kFastWaves * 64) void decode_fast_kernel(DecodeArgs a) {
-  Fast<QS, KS, GT, BS, kFastWaves>::run(a);
+template <typename QS, typename KS, int GT, int BS, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_fast_kernel(DecodeArgs a) {
+  Fast<QS, KS, GT, BS, NW>::run(a);
 }
 
 template <typename QS, typename KS, int GT, int BS>
@@ -1482,12 +1486,23 @@ hipError_t launch_fast_bs(const DecodeArgs &a, hipStream_t s) {
     }
   }
   const dim3 grid(a.partition_size > 0 ? a.max_parts : 1, a.num_kv_heads * a.head_groups, a.num_seqs);
+  if (a.partition_size > 0) {
+    const dim3 block(kSplitWaves * 64);
+    switch (a.heads_per_wg) {
+      case 1: hipLaunchKernelGGL((decode_fast_kernel<QS, KS, 1, BS, kSplitWaves>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((decode_fast_kernel<QS, KS, 2, BS, kSplitWaves>), grid, block, 0, s, a); break;
+      case 4: hipLaunchKernelGGL((decode_fast_kernel<QS, KS, 4, BS, kSplitWaves>), grid, block, 0, s, a); break;
+      case 8: hipLaunchKernelGGL((decode_fast_kernel<QS, KS, 8, BS, kSplitWaves>), grid, block, 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   const dim3 block(kFastWaves * 64);
   switch (a.heads_per_wg) {
-    case 1: hipLaunchKernelGGL((decode_fast_kernel<QS, KS, 1, BS>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_fast_kernel<QS, KS, 2, BS>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_fast_kernel<QS, KS, 4, BS>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((decode_fast_kernel<QS, KS, 8, BS>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((decode_fast_kernel<QS, KS, 1, BS, kFastWaves>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_fast_kernel<QS, KS, 2, BS, kFastWaves>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_fast_kernel<QS, KS, 4, BS, kFastWaves>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((decode_fast_kernel<QS, KS, 8, BS, kFastWaves>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
