@@ -181,10 +181,12 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *                 leading bytes hold counters, which MUST be zero before the
  *                 first call that uses the workspace: zero-fill the whole
  *                 workspace once when it is allocated.  Every call leaves
- *                 the counters zero again; the rest may hold anything.  Calls
- *                 that may run concurrently must not share one workspace,
- *                 and a workspace serves one partition mode (zero-fill it
- *                 again before switching).  The balanced split relies on
+ *                 the counters zero again; the rest may hold anything.  One
+ *                 workspace, sized for the largest batch, serves calls with
+ *                 any number of sequences; it serves one partition mode and
+ *                 one head layout (head_dim, query heads per KV head): zero-
+ *                 fill it again before switching.  Calls that may run
+ *                 concurrently must not share one workspace.  The balanced split relies on
  *                 the dispatcher dealing workgroups to the XCDs in turn; a
  *                 launch that finds otherwise writes NaN rows and marks the
  *                 workspace, and every later call with a marked workspace

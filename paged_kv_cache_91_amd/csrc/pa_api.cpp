@@ -264,10 +264,14 @@ int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
     a.stream_waves = static_cast<int32_t>(w.stream_waves);
     a.num_xcd = static_cast<int32_t>(w.num_xcd);
     a.share_ranges = static_cast<int32_t>(w.share_ranges);
+    // control words, then the partial slots (their size does not depend on
+    // the batch), then a counter line per (sequence, head group): unit u's
+    // line sits at the same offset whatever the number of sequences, so one
+    // zero-filled workspace serves batches of any size
     char *base = static_cast<char *>(workspace);
     a.ctl = reinterpret_cast<int32_t *>(base);
-    a.counters = reinterpret_cast<int32_t *>(base + w.ctl_bytes);
-    float *ws = reinterpret_cast<float *>(base + w.ctl_bytes + w.counter_bytes);
+    float *ws = reinterpret_cast<float *>(base + w.ctl_bytes);
+    a.counters = reinterpret_cast<int32_t *>(base + w.ctl_bytes + w.partial_floats * 4);
     const int64_t slots = w.num_xcd * w.share_ranges * 2;
     a.part_o = ws;                                     // [share][range][side][head][D]
     a.part_m = ws + slots * hpw * pool->head_dim;      // [share][range][side][32]: (m, l) per head

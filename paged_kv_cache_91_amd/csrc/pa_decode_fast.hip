@@ -1440,6 +1440,15 @@ struct Fast {
 constexpr int kFastWaves = 4;
 constexpr int kSplitWaves = 1;
 
+// Zeroes the split's arrival counters of this call's (sequence, head group)
+// units before the decode launch, so that a workspace whose bytes earlier
+// calls used for other things (partials of a larger batch) still starts the
+// count at zero.  A kernel rather than a memset keeps the call capturable.
+__global__ __launch_bounds__(256) void zero_counters_kernel(int32_t *c, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) c[i] = 0;
+}
+
 template <typename QS, typename KS, int GT, int BS, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_fast_kernel(DecodeArgs a) {
   Fast<QS, KS, GT, BS, NW>::run(a);
@@ -1487,6 +1496,9 @@ hipError_t launch_fast_bs(const DecodeArgs &a, hipStream_t s) {
   }
   const dim3 grid(a.partition_size > 0 ? a.max_parts : 1, a.num_kv_heads * a.head_groups, a.num_seqs);
   if (a.partition_size > 0) {
+    const int64_t units = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * a.head_groups;
+    hipLaunchKernelGGL(zero_counters_kernel, dim3(static_cast<unsigned>((units + 255) / 256)), dim3(256), 0, s,
+                       a.counters, units);
     const dim3 block(kSplitWaves * 64);
     switch (a.heads_per_wg) {
       case 1: hipLaunchKernelGGL((decode_fast_kernel<QS, KS, 1, BS, kSplitWaves>), grid, block, 0, s, a); break;

@@ -389,3 +389,34 @@ def test_placement_check_marks_workspace_until_zeroed(surplus):
     ws.zero_()
     for _ in range(2):
         assert max_err(_auto(dev, ws), ref) <= 2e-2
+
+
+@pytest.mark.parametrize("part", [pa.PA_PARTITION_AUTO, 64])
+def test_workspace_reused_across_batches(part):
+    """One workspace, sized for the largest, through calls on different
+    batches (different numbers of sequences, tiles and split units): each
+    call finds its counters at zero although earlier calls used the same
+    bytes differently, and each result matches the oracle and repeats bit for
+    bit."""
+    wls = [W.config2(seed=61, num_seqs=7, ctx_range=(1, 700), num_blocks=400),
+           W.config2(seed=62, num_seqs=3, ctx_range=(300, 1200), num_blocks=300),
+           W.config2(seed=63, num_seqs=12, ctx_range=(1, 90), num_blocks=100)]
+    sizes = [pa.pa_decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                          w.max_blocks_per_seq, w.block_size, part)
+             for w in wls]
+    ws = torch.zeros(max(sizes), dtype=torch.uint8, device=DEV)
+    devs = [DeviceWorkload(w) for w in wls]
+    refs = [oracle_out(w) for w in wls]
+    first = [None] * len(wls)
+    for rnd in range(3):
+        for i, (w, dev) in enumerate(zip(wls, devs)):
+            out = torch.full_like(dev.q, float("nan"))
+            got = out_f64(pa.pa_decode(dev.q, dev.pool, dev.tables, dev.ctx, w.scale, out=out,
+                                       partition_size=part, workspace=ws, q_dtype=w.q_dtype))
+            assert max_err(got, refs[i]) <= 2e-2, (rnd, i)
+            if first[i] is None:
+                first[i] = got
+            else:
+                assert np.array_equal(got, first[i]), (rnd, i)
+    if part == pa.PA_PARTITION_AUTO:
+        assert int(ws.view(torch.int32)[32 * 17].item()) == 0  # never marked
