@@ -221,6 +221,20 @@ const char *pa_last_error(void);
 /* Library version, major * 10000 + minor * 100 + patch. */
 int pa_version(void);
 
+/*
+ * pa_time_next_decode -- benchmark hook.  The calling thread's next
+ * pa_decode records start_event as its first kernel begins and stop_event as
+ * its last kernel ends (the event pair of hipExtLaunchKernel), so that the
+ * pair brackets the decode kernels alone, not the stream's other commands.
+ * The pair applies to that one call, whatever its outcome (a call that fails
+ * validation or enqueues nothing records neither event).
+ *
+ *   start_event, stop_event  hipEvent_t handles the caller created with
+ *                            timing enabled; both NULL clears a pending pair.
+ * Returns PA_OK, or PA_ERR_INVALID_ARG when exactly one of them is NULL.
+ */
+int pa_time_next_decode(void *start_event, void *stop_event);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,6 +18,8 @@
 namespace {
 
 thread_local char g_last_error[256] = "";
+// the event pair pa_time_next_decode set for this thread's next pa_decode
+thread_local pa_impl::LaunchEvents g_next_events;
 
 int fail(int status, const char *fmt, ...) {
   va_list ap;
@@ -143,6 +145,14 @@ const char *pa_last_error(void) { return g_last_error; }
 
 int pa_version(void) { return 100; }
 
+int pa_time_next_decode(void *start_event, void *stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(PA_ERR_INVALID_ARG, "pa_time_next_decode: give both events or neither");
+  g_next_events.start = static_cast<hipEvent_t>(start_event);
+  g_next_events.stop = static_cast<hipEvent_t>(stop_event);
+  return ok();
+}
+
 int pa_write_kv(const void *k, const void *v, int32_t src_dtype, int32_t num_tokens,
                 const int64_t *slot_mapping, const pa_kv_pool *pool, pa_stream_t stream) {
   if (int st = check_pool(pool)) return st;
@@ -191,6 +201,8 @@ int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
               const pa_kv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
               const int32_t *context_lens, float scale, void *out, int32_t partition_size,
               void *workspace, size_t workspace_bytes, pa_stream_t stream) {
+  const pa_impl::LaunchEvents ev = g_next_events;    // the pair applies to this call only
+  g_next_events = pa_impl::LaunchEvents{};
   if (int st = check_pool(pool)) return st;
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 0");
   if (num_seqs == 0) return ok();
@@ -300,12 +312,15 @@ int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
     }
   }
   hipError_t e;
+  const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (fast) {
-    e = pa_impl::launch_decode_fast(q_dtype, pool->dtype, a, reinterpret_cast<hipStream_t>(stream));
+    e = pa_impl::launch_decode_fast(q_dtype, pool->dtype, a, hs, ev);
   } else {
     bool supported = true;
-    e = pa_impl::launch_decode(q_dtype, pool->dtype, a, reinterpret_cast<hipStream_t>(stream), &supported);
+    if (ev.start && (e = hipEventRecord(ev.start, hs)) != hipSuccess) return hip_fail(e);
+    e = pa_impl::launch_decode(q_dtype, pool->dtype, a, hs, &supported);
     if (!supported) return fail(PA_ERR_UNSUPPORTED, "decode specialisation not built");
+    if (e == hipSuccess && ev.stop) e = hipEventRecord(ev.stop, hs);
   }
   if (e != hipSuccess) return hip_fail(e);
   return ok();

@@ -44,6 +44,7 @@
 // and resets the counter to zero for the next call.  The result does not
 // depend on which partition finishes last.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -1465,7 +1466,7 @@ __global__ __launch_bounds__(512) void decode_pair_kernel(DecodeArgs a) {
 // compute unit has, which keeps a second workgroup off the same unit.
 constexpr int kPairLdsBytes = 84 * 1024;
 template <typename QS, typename KS, int GT, int BS>
-hipError_t launch_stream_gt(const DecodeArgs &a, hipStream_t s) {
+hipError_t launch_stream_gt(const DecodeArgs &a, hipStream_t s, const LaunchEvents &ev) {
   static const int fixed = [] {
     hipFuncAttributes at{};
     if (hipFuncGetAttributes(&at, reinterpret_cast<const void *>(&decode_pair_kernel<QS, KS, GT, BS>)) !=
@@ -1479,50 +1480,50 @@ hipError_t launch_stream_gt(const DecodeArgs &a, hipStream_t s) {
   // range codes (4 bytes per range), at least up to kPairLdsBytes in all
   const int table = (4 * wgs + 1) * 8 + 4 * wgs * 4;
   const int dyn = max(table, kPairLdsBytes - fixed);
-  hipLaunchKernelGGL((decode_pair_kernel<QS, KS, GT, BS>), dim3(wgs), dim3(512), dyn, s, a);
+  hipExtLaunchKernelGGL((decode_pair_kernel<QS, KS, GT, BS>), dim3(wgs), dim3(512), dyn, s, ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 
 template <typename QS, typename KS, int BS>
-hipError_t launch_fast_bs(const DecodeArgs &a, hipStream_t s) {
+hipError_t launch_fast_bs(const DecodeArgs &a, hipStream_t s, const LaunchEvents &ev) {
   if (a.stream_waves > 0) {
     switch (a.heads_per_wg) {
-      case 1: return launch_stream_gt<QS, KS, 1, BS>(a, s);
-      case 2: return launch_stream_gt<QS, KS, 2, BS>(a, s);
-      case 4: return launch_stream_gt<QS, KS, 4, BS>(a, s);
-      case 8: return launch_stream_gt<QS, KS, 8, BS>(a, s);
+      case 1: return launch_stream_gt<QS, KS, 1, BS>(a, s, ev);
+      case 2: return launch_stream_gt<QS, KS, 2, BS>(a, s, ev);
+      case 4: return launch_stream_gt<QS, KS, 4, BS>(a, s, ev);
+      case 8: return launch_stream_gt<QS, KS, 8, BS>(a, s, ev);
       default: return hipErrorInvalidValue;
     }
   }
   const dim3 grid(a.partition_size > 0 ? a.max_parts : 1, a.num_kv_heads * a.head_groups, a.num_seqs);
   if (a.partition_size > 0) {
     const int64_t units = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * a.head_groups;
-    hipLaunchKernelGGL(zero_counters_kernel, dim3(static_cast<unsigned>((units + 255) / 256)), dim3(256), 0, s,
-                       a.counters, units);
+    hipExtLaunchKernelGGL(zero_counters_kernel, dim3(static_cast<unsigned>((units + 255) / 256)), dim3(256), 0, s,
+                          ev.start, nullptr, 0, a.counters, units);
     const dim3 block(kSplitWaves * 64);
     switch (a.heads_per_wg) {
-      case 1: hipLaunchKernelGGL((decode_fast_kernel<QS, KS, 1, BS, kSplitWaves>), grid, block, 0, s, a); break;
-      case 2: hipLaunchKernelGGL((decode_fast_kernel<QS, KS, 2, BS, kSplitWaves>), grid, block, 0, s, a); break;
-      case 4: hipLaunchKernelGGL((decode_fast_kernel<QS, KS, 4, BS, kSplitWaves>), grid, block, 0, s, a); break;
-      case 8: hipLaunchKernelGGL((decode_fast_kernel<QS, KS, 8, BS, kSplitWaves>), grid, block, 0, s, a); break;
+#define PA_SPLIT(G) \
+      case G: hipExtLaunchKernelGGL((decode_fast_kernel<QS, KS, G, BS, kSplitWaves>), grid, block, 0, s, nullptr, ev.stop, 0, a); break;
+      PA_SPLIT(1) PA_SPLIT(2) PA_SPLIT(4) PA_SPLIT(8)
+#undef PA_SPLIT
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }
   const dim3 block(kFastWaves * 64);
   switch (a.heads_per_wg) {
-    case 1: hipLaunchKernelGGL((decode_fast_kernel<QS, KS, 1, BS, kFastWaves>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_fast_kernel<QS, KS, 2, BS, kFastWaves>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_fast_kernel<QS, KS, 4, BS, kFastWaves>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((decode_fast_kernel<QS, KS, 8, BS, kFastWaves>), grid, block, 0, s, a); break;
+#define PA_SINGLE(G) \
+    case G: hipExtLaunchKernelGGL((decode_fast_kernel<QS, KS, G, BS, kFastWaves>), grid, block, 0, s, ev.start, ev.stop, 0, a); break;
+    PA_SINGLE(1) PA_SINGLE(2) PA_SINGLE(4) PA_SINGLE(8)
+#undef PA_SINGLE
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <typename QS, typename KS>
-hipError_t launch_fast_t(const DecodeArgs &a, hipStream_t s) {
-  return a.block_size == 16 ? launch_fast_bs<QS, KS, 16>(a, s) : launch_fast_bs<QS, KS, 32>(a, s);
+hipError_t launch_fast_t(const DecodeArgs &a, hipStream_t s, const LaunchEvents &ev) {
+  return a.block_size == 16 ? launch_fast_bs<QS, KS, 16>(a, s, ev) : launch_fast_bs<QS, KS, 32>(a, s, ev);
 }
 
 }  // namespace
@@ -1533,11 +1534,12 @@ bool fast_decode_applies(int q_dtype, int kv_dtype, const DecodeArgs &a) {
   return kv_dtype == q_dtype || kv_dtype == kFP8;
 }
 
-hipError_t launch_decode_fast(int q_dtype, int kv_dtype, const DecodeArgs &a, hipStream_t s) {
-  if (q_dtype == kBF16 && kv_dtype == kBF16) return launch_fast_t<BF16S, BF16S>(a, s);
-  if (q_dtype == kF16 && kv_dtype == kF16) return launch_fast_t<F16S, F16S>(a, s);
-  if (q_dtype == kBF16 && kv_dtype == kFP8) return launch_fast_t<BF16S, FP8S>(a, s);
-  if (q_dtype == kF16 && kv_dtype == kFP8) return launch_fast_t<F16S, FP8S>(a, s);
+hipError_t launch_decode_fast(int q_dtype, int kv_dtype, const DecodeArgs &a, hipStream_t s,
+                              const LaunchEvents &ev) {
+  if (q_dtype == kBF16 && kv_dtype == kBF16) return launch_fast_t<BF16S, BF16S>(a, s, ev);
+  if (q_dtype == kF16 && kv_dtype == kF16) return launch_fast_t<F16S, F16S>(a, s, ev);
+  if (q_dtype == kBF16 && kv_dtype == kFP8) return launch_fast_t<BF16S, FP8S>(a, s, ev);
+  if (q_dtype == kF16 && kv_dtype == kFP8) return launch_fast_t<F16S, FP8S>(a, s, ev);
   return hipErrorInvalidValue;
 }
 

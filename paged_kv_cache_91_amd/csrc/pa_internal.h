@@ -77,7 +77,14 @@ hipError_t launch_copy(const CopyArgs &a, hipStream_t s);
 // head_dim 128 decode with matrix-core q.K^T and the fused split merge
 // (pa_decode_fast.hip); fast_decode_applies() says whether it covers a call.
 bool fast_decode_applies(int q_dtype, int kv_dtype, const DecodeArgs &a);
-hipError_t launch_decode_fast(int q_dtype, int kv_dtype, const DecodeArgs &a, hipStream_t s);
+// Events the launch records as its first kernel begins and its last kernel
+// ends (none when null).
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+hipError_t launch_decode_fast(int q_dtype, int kv_dtype, const DecodeArgs &a, hipStream_t s,
+                              const LaunchEvents &ev);
 
 // Compute units of the current device (256 when it cannot be queried, e.g.
 // on a machine without a GPU, where only sizes are computed).

@@ -30,7 +30,7 @@ _TORCH_STORAGE = {PA_F32: (torch.float32,), PA_F16: (torch.float16,),
 _ELEM = {PA_F32: 4, PA_F16: 2, PA_BF16: 2, PA_FP8_E4M3: 1}
 
 EXPORTED = ("pa_write_kv", "pa_decode", "pa_decode_workspace_bytes", "pa_copy_blocks",
-            "pa_status_string", "pa_last_error", "pa_version")
+            "pa_status_string", "pa_last_error", "pa_version", "pa_time_next_decode")
 
 
 class PaError(RuntimeError):
@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
         L.pa_last_error.restype = ctypes.c_char_p
         L.pa_version.argtypes = []
         L.pa_version.restype = ctypes.c_int
+        L.pa_time_next_decode.argtypes = [vp, vp]
+        L.pa_time_next_decode.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -214,3 +216,13 @@ def pa_copy_blocks(pool: KvPool, src_dst_pairs: torch.Tensor, stream=None) -> No
     _check(lib().pa_copy_blocks(ctypes.byref(pool), _ptr(src_dst_pairs, "src_dst_pairs") if num else None,
                                 num, _stream(stream)),
            "pa_copy_blocks")
+
+
+def pa_time_next_decode(start, stop) -> None:
+    """Have the next pa_decode on this thread record ``start`` / ``stop``
+    (timing-enabled torch.cuda.Event objects, already recorded once so that
+    they exist) as its kernels begin and end."""
+    if (start is None) != (stop is None):
+        raise ValueError("give both events or neither")
+    _check(lib().pa_time_next_decode(None if start is None else start.cuda_event,
+                                     None if stop is None else stop.cuda_event), "pa_time_next_decode")

@@ -136,3 +136,14 @@ def test_write_and_copy_validation():
     assert lib.pa_copy_blocks(ctypes.byref(p), FAKE, 0, None) == 0
     assert lib.pa_copy_blocks(ctypes.byref(p), None, 3, None) == -1
     assert lib.pa_copy_blocks(None, FAKE, 3, None) == -1
+
+
+def test_time_next_decode_validation():
+    lib = pa.lib()
+    assert lib.pa_time_next_decode(FAKE, None) == -1
+    assert lib.pa_time_next_decode(None, FAKE) == -1
+    assert lib.pa_time_next_decode(None, None) == 0
+    # a pair set and then consumed by a call that fails validation is gone
+    assert lib.pa_time_next_decode(FAKE, FAKE * 2) == 0
+    assert _decode(_pool(block_size=3)) == -1
+    assert _decode(_pool(), num_seqs=0) == 0

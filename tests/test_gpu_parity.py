@@ -420,3 +420,31 @@ def test_workspace_reused_across_batches(part):
                 assert np.array_equal(got, first[i]), (rnd, i)
     if part == pa.PA_PARTITION_AUTO:
         assert int(ws.view(torch.int32)[32 * 17].item()) == 0  # never marked
+
+
+@pytest.mark.parametrize("part", [pa.PA_PARTITION_AUTO, 0, 64])
+def test_timed_decode_records_its_kernels(part):
+    """pa_time_next_decode: the event pair brackets the call's kernels (a
+    positive time no longer than a bracket around the whole call) and the
+    result is unchanged."""
+    wl = W.config2(seed=71, num_seqs=5, ctx_range=(50, 900), num_blocks=300)
+    dev = DeviceWorkload(wl)
+    ref = oracle_out(wl)
+    st = torch.cuda.current_stream()
+    k0, k1, b0, b1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    for e in (k0, k1):
+        e.record(st)                   # creates the events
+    torch.cuda.synchronize()
+    ws = pa.new_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.max_blocks_per_seq,
+                          wl.block_size, part, device=DEV) if part else None
+    out = torch.full_like(dev.q, float("nan"))
+    b0.record(st)
+    pa.pa_time_next_decode(k0, k1)
+    pa.pa_decode(dev.q, dev.pool, dev.tables, dev.ctx, wl.scale, out=out, partition_size=part,
+                 workspace=ws, q_dtype=wl.q_dtype, stream=st)
+    b1.record(st)
+    torch.cuda.synchronize()
+    kernel_ms, bracket_ms = k0.elapsed_time(k1), b0.elapsed_time(b1)
+    say(f"    partition {part}: kernels {kernel_ms * 1e3:.1f} us, bracket {bracket_ms * 1e3:.1f} us")
+    assert 0 < kernel_ms <= bracket_ms
+    assert max_err(out_f64(out), ref) <= 2e-2
