@@ -705,10 +705,22 @@ struct Fast {
     f32x2_t ml[GT];
     int64_t unit, gu, row0;
     int nts, hcount, split, side;
+    int taken;                     // claimed for handling (by the helper, or by the streamer for its last entry)
   };
   struct Box {
     Mail m[kMail];
     int head, tail, done, pad;     // posted (streamer), taken (helper); streamer finished
+  };
+
+  // The unit a range ends inside, when the range cuts it, worked out while
+  // the range streams: its holder count and partial slots (tile order), so
+  // that the merge at the range's end, the one on the kernel's critical
+  // path, needs no table walk and issues all its loads at once.
+  static constexpr int kPre = 8;
+  struct Pre {
+    bool on, cross;
+    int64_t unit, count;
+    int64_t slot[kPre];
   };
 
   // total tiles T of the batch; n_lane / cnt0 / incl0: the first 64
@@ -802,7 +814,8 @@ struct Fast {
   static __device__ void run_pair(const DecodeArgs &a) {
     __shared__ Box box[4];
     __shared__ uint4 s_q[4][kQSlots][GT * 16];
-    __shared__ int s_reg, s_poison, s_tbl;
+    __shared__ int s_reg, s_poison, s_tbl, s_preok;
+    __shared__ Pre s_pre[4];
     // dynamic LDS: the table of range starts (the helpers' lookups)
     extern __shared__ int64_t pa_dyn_lds[];
     const int wave = uniform(static_cast<int>(threadIdx.x >> 6));
@@ -828,6 +841,7 @@ struct Fast {
       s_reg = reg_got;
       s_poison = poison_got;
       s_tbl = 0;
+      s_preok = 0;
     }
     if (lane == 0) {
       if (helper) {
@@ -867,20 +881,38 @@ struct Fast {
       }
     }
     const Share sh = share_geom(T, NX, x);
+    const int64_t NR = 4 * static_cast<int64_t>(gridDim.x);
+    int64_t *rs = pa_dyn_lds;
+    int *rc = reinterpret_cast<int *>(pa_dyn_lds + NR + 1);
     if (!helper) {
       int64_t lo, hi;
       range_of(sh, 4 * reg + slot, lo, hi);
       if (lo < hi) stream(a, bx, s_q[slot], lo, hi, lane, n_lane, cnt0, incl0);
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       if (lane == 0) lds_put(&bx.done, 1);
+      // the range's last segment, unless the helper already took it: the
+      // helper may still be merging the segment before, and this is the
+      // merge on the launch's critical path
+      const int last = lds_get(&bx.head) - 1;
+      if (last >= 0) {
+        int won = 0;
+        if (lane == 0) {
+          int expect = 0;
+          won = __hip_atomic_compare_exchange_strong(&bx.m[last % kMail].taken, &expect, 1, __ATOMIC_RELAXED,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        if (uniform(won) != 0) {
+          while (lds_get(&s_tbl) < 4 || lds_get(&s_preok) < 4) __builtin_amdgcn_s_sleep(1);
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          Pre pre = s_pre[slot];
+          handle(a, T, x * (a.share_ranges) + 4 * reg + slot, bx.m[last % kMail], lane, rs, rc, pre);
+        }
+      }
       return;
     }
     // The helpers fill the table of range starts: rs[r] for the batch's
     // ranges in tile order (r < NR, share by share), rs[NR] = T, and for
     // each range its share y and index i in the share, as (y << 20) | i.
-    const int64_t NR = 4 * static_cast<int64_t>(gridDim.x);
-    int64_t *rs = pa_dyn_lds;
-    int *rc = reinterpret_cast<int *>(pa_dyn_lds + NR + 1);
     {
       const int64_t q = static_cast<int64_t>(gridDim.x) / NX, rr = static_cast<int64_t>(gridDim.x) - q * NX;
       for (int64_t r = (wave - 4) * 64 + lane; r <= NR; r += 256) {
@@ -904,7 +936,8 @@ struct Fast {
     }
     int64_t lo, hi;
     range_of(sh, 4 * reg + slot, lo, hi);
-    helper_main(a, bx, T, x * (a.share_ranges) + 4 * reg + slot, lo, hi, lane, n_lane, cnt0, incl0, rs, rc);
+    helper_main(a, bx, T, x * (a.share_ranges) + 4 * reg + slot, lo, hi, lane, n_lane, cnt0, incl0, rs, rc,
+                s_pre[slot], s_preok);
   }
 
   // The streamer's tile range [lo, hi) of the T-tile list.  Finished
@@ -1064,6 +1097,7 @@ struct Fast {
               e.nts = cc.nts;
               e.hcount = hcount;
               e.row0 = row0;
+              e.taken = 0;
             }
             ++head;
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -1084,7 +1118,7 @@ struct Fast {
   // sequences, then the mailbox until the streamer is done.
   static __device__ void helper_main(const DecodeArgs &a, Box &bx, int64_t T, int64_t rid, int64_t lo, int64_t hi,
                                      int lane, int n_lane, int64_t cnt0, int64_t incl0, const int64_t *rs,
-                                     const int *rc) {
+                                     const int *rc, Pre &s_pre_own, int &s_preok) {
     const int64_t nh = 4 * static_cast<int64_t>(gridDim.x);
     const int maxn = a.max_blocks * BS;
     const int hid = static_cast<int>(threadIdx.x >> 6) - 4;
@@ -1125,13 +1159,24 @@ struct Fast {
       }
     }
 
+    // the streamer handles its last entry itself when it gets there first
+    if (lane == 0) s_pre_own = pre;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (lane == 0) __hip_atomic_fetch_add(&s_preok, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+
     int tail = 0;
     for (;;) {
       const int done = lds_get(&bx.done);
       const int head = lds_get(&bx.head);
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       if (tail < head) {
-        handle(a, T, rid, bx.m[tail % kMail], lane, rs, rc, pre);
+        int won = 0;
+        if (lane == 0) {
+          int expect = 0;
+          won = __hip_atomic_compare_exchange_strong(&bx.m[tail % kMail].taken, &expect, 1, __ATOMIC_RELAXED,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        if (uniform(won) != 0) handle(a, T, rid, bx.m[tail % kMail], lane, rs, rc, pre);
         ++tail;
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         if (lane == 0) lds_put(&bx.tail, tail);
@@ -1161,16 +1206,6 @@ struct Fast {
       }
   }
 
-  // The unit a range ends inside, when the range cuts it, worked out while
-  // the range streams: its holder count and partial slots (tile order), so
-  // that the merge at the range's end, the one on the kernel's critical
-  // path, needs no table walk and issues all its loads at once.
-  static constexpr int kPre = 8;
-  struct Pre {
-    bool on, cross;
-    int64_t unit, count;
-    int64_t slot[kPre];
-  };
 
   // The helper's work for one mailbox entry of the streamer with range index
   // `rid`.  A whole unit: its output rows.  A split unit: the range's partial
