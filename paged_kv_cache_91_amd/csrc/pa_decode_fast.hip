@@ -657,7 +657,10 @@ struct Fast {
   // whole unit's outputs, or a range's partial for a unit split between
   // ranges) goes to the helper through an LDS mailbox; the helper writes the
   // rows, publishes the partials, counts them in and merges the split units
-  // while its streamer keeps streaming.
+  // while its streamer keeps streaming.  The range's last segment is taken
+  // by whichever of the pair gets to it first (a compare-and-swap on the
+  // entry): usually the streamer, once its stream is over, since the helper
+  // may still be merging the segment before.
   //
   // Exchange.  The partials of a unit inside one share are written and
   // merged by waves of one XCD, so they go through that XCD's L2 with
