@@ -31,6 +31,9 @@ FLAGS = [
     # adds accumulation registers on top of ~200 VGPRs, which halves how many
     # decode waves a SIMD holds
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # the first scalar kernel arguments arrive preloaded in SGPRs rather than
+    # through a load of the argument block at the start of every wave
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I" + os.path.join(ROOT, "include"),
     "-I" + os.path.join(PKG, "csrc"),
 ]

@@ -1494,7 +1494,20 @@ __global__ __launch_bounds__(NW * 64) void decode_fast_kernel(DecodeArgs a) {
 }
 
 template <typename QS, typename KS, int GT, int BS>
-__global__ __launch_bounds__(512) void decode_pair_kernel(DecodeArgs a) {
+// The fields the launch's first loads depend on come as separate scalar
+// arguments ahead of the struct, so that they can arrive preloaded in SGPRs
+// (kernel-argument preloading) instead of through a load of the argument
+// block.
+__global__ __launch_bounds__(512) void decode_pair_kernel(const int32_t *ctx, int32_t *ctl, int32_t num_seqs,
+                                                          int32_t max_blocks, int32_t num_kv_heads,
+                                                          int32_t head_groups, int32_t num_xcd, DecodeArgs a) {
+  a.ctx = ctx;
+  a.ctl = ctl;
+  a.num_seqs = num_seqs;
+  a.max_blocks = max_blocks;
+  a.num_kv_heads = num_kv_heads;
+  a.head_groups = head_groups;
+  a.num_xcd = num_xcd;
   Fast<QS, KS, GT, BS, 1>::run_pair(a);
 }
 
@@ -1518,7 +1531,8 @@ hipError_t launch_stream_gt(const DecodeArgs &a, hipStream_t s, const LaunchEven
   // range codes (4 bytes per range), at least up to kPairLdsBytes in all
   const int table = (4 * wgs + 1) * 8 + 4 * wgs * 4;
   const int dyn = max(table, kPairLdsBytes - fixed);
-  hipExtLaunchKernelGGL((decode_pair_kernel<QS, KS, GT, BS>), dim3(wgs), dim3(512), dyn, s, ev.start, ev.stop, 0, a);
+  hipExtLaunchKernelGGL((decode_pair_kernel<QS, KS, GT, BS>), dim3(wgs), dim3(512), dyn, s, ev.start, ev.stop, 0,
+                        a.ctx, a.ctl, a.num_seqs, a.max_blocks, a.num_kv_heads, a.head_groups, a.num_xcd, a);
   return hipGetLastError();
 }
 
