@@ -239,6 +239,28 @@ __device__ __forceinline__ int64_t uniform(int64_t x) {
   return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
+// lane l's value, l uniform: two lane reads rather than an LDS permute
+__device__ __forceinline__ int64_t lane_value(int64_t x, int l) {
+  const uint64_t u = static_cast<uint64_t>(x);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(u), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(u >> 32), l);
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Inclusive sum over the wave's 64 lanes of 32-bit values, with DPP moves
+// (no LDS): shifts by 1, 2, 4 and 8 within each row of 16 lanes, then each
+// row's last lane added into the rows after it (row broadcasts of lanes 15
+// and 31).  Lanes a move has no source for contribute 0.
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -728,6 +750,8 @@ struct Fast {
 
   // total tiles T of the batch; n_lane / cnt0 / incl0: the first 64
   // sequences' lengths, tile counts and inclusive running sums, one per lane
+  // context lengths below which 64 sequences' tile counts fit 32 bits
+  static constexpr int kScan32 = 1 << 28;
   static __device__ __forceinline__ int64_t count_tiles(const DecodeArgs &a, int lane, int &n_lane,
                                                         int64_t &cnt0, int64_t &incl0) {
     const int S = a.num_seqs;
@@ -735,18 +759,29 @@ struct Fast {
     const int maxn = a.max_blocks * BS;
     n_lane = lane < S ? a.ctx[lane] : 0;
     cnt0 = tiles_of(n_lane, maxn);
-    incl0 = cnt0;
+    int64_t T;
+    if (maxn < kScan32) {
+      // 64 sequences' tiles fit 32 bits: a DPP scan
+      incl0 = wave_incl_sum(static_cast<uint32_t>(cnt0));
+      T = lane_value(incl0, 63);
+      for (int c0 = 64; c0 < S; c0 += 64) {
+        const uint32_t cnt = (c0 + lane < S) ? static_cast<uint32_t>(tiles_of(a.ctx[c0 + lane], maxn)) : 0u;
+        T += __builtin_amdgcn_readlane(wave_incl_sum(cnt), 63);
+      }
+    } else {
+      incl0 = cnt0;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int64_t up = __shfl_up(incl0, o, 64);
-      if (lane >= o) incl0 += up;
-    }
-    int64_t T = uniform(__shfl(incl0, 63, 64));
-    for (int c0 = 64; c0 < S; c0 += 64) {
-      int64_t cnt = (c0 + lane < S) ? tiles_of(a.ctx[c0 + lane], maxn) : 0;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int64_t up = __shfl_up(incl0, o, 64);
+        if (lane >= o) incl0 += up;
+      }
+      T = lane_value(incl0, 63);
+      for (int c0 = 64; c0 < S; c0 += 64) {
+        int64_t cnt = (c0 + lane < S) ? tiles_of(a.ctx[c0 + lane], maxn) : 0;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) cnt += __shfl_xor(cnt, o, 64);
-      T += cnt;
+        for (int o = 1; o < 64; o <<= 1) cnt += __shfl_xor(cnt, o, 64);
+        T += cnt;
+      }
     }
     return uniform(T * KVG);
   }
@@ -759,27 +794,34 @@ struct Fast {
     const int maxn = a.max_blocks * BS;
     int s = 0, n0 = 0;
     int64_t G = 0;                     // first global tile of sequence s
-    const int64_t total0 = uniform(__shfl(incl0, 63, 64)) * KVG;
+    const int64_t total0 = lane_value(incl0, 63) * KVG;
     if (total0 > g) {
-      const int first = __builtin_ctzll(__builtin_amdgcn_ballot_w64(incl0 * KVG > g));
-      s = uniform(first);
-      G = uniform((__shfl(incl0, first, 64) - __shfl(cnt0, first, 64)) * KVG);
+      const int first = uniform(static_cast<int>(__builtin_ctzll(__builtin_amdgcn_ballot_w64(incl0 * KVG > g))));
+      s = first;
+      G = (lane_value(incl0, first) - lane_value(cnt0, first)) * KVG;
       n0 = __builtin_amdgcn_readlane(n_lane, first);
     } else {
       int64_t base = total0;
       for (int c0 = 64; c0 < S; c0 += 64) {
-        const int64_t cnt = ((c0 + lane < S) ? tiles_of(a.ctx[c0 + lane], maxn) : 0) * static_cast<int64_t>(KVG);
-        int64_t incl = cnt;
+        const int64_t t = (c0 + lane < S) ? tiles_of(a.ctx[c0 + lane], maxn) : 0;
+        int64_t incl;
+        if (maxn < kScan32) {
+          incl = wave_incl_sum(static_cast<uint32_t>(t));
+        } else {
+          incl = t;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int64_t up = __shfl_up(incl, o, 64);
-          if (lane >= o) incl += up;
+          for (int o = 1; o < 64; o <<= 1) {
+            const int64_t up = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += up;
+          }
         }
-        const int64_t total = uniform(__shfl(incl, 63, 64));
+        const int64_t cnt = t * KVG;
+        incl *= KVG;
+        const int64_t total = lane_value(incl, 63);
         if (base + total > g) {
-          const int first = __builtin_ctzll(__builtin_amdgcn_ballot_w64(base + incl > g));
-          s = uniform(c0 + first);
-          G = uniform(base + __shfl(incl, first, 64) - __shfl(cnt, first, 64));
+          const int first = uniform(static_cast<int>(__builtin_ctzll(__builtin_amdgcn_ballot_w64(base + incl > g))));
+          s = c0 + first;
+          G = base + lane_value(incl, first) - lane_value(cnt, first);
           n0 = load_const(a.ctx, s);
           break;
         }
