@@ -708,7 +708,7 @@ struct Fast {
 
   // workgroups the dispatcher places on XCD x, and share x's tiles and ranges
   static __device__ __forceinline__ int64_t wgs_on(int64_t x, int NX) {
-    return (static_cast<int64_t>(gridDim.x) - x + NX - 1) / NX;
+    return (gridDim.x - static_cast<uint32_t>(x) + static_cast<uint32_t>(NX) - 1) / static_cast<uint32_t>(NX);
   }
   struct Share {
     int64_t X0, X1, nr;   // tiles [X0, X1) in nr ranges
