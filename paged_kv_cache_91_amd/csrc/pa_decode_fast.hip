@@ -950,7 +950,7 @@ struct Fast {
           while (lds_get(&s_tbl) < 4 || lds_get(&s_preok) < 4) __builtin_amdgcn_s_sleep(1);
           __atomic_signal_fence(__ATOMIC_SEQ_CST);
           Pre pre = s_pre[slot];
-          handle(a, T, x * (a.share_ranges) + 4 * reg + slot, bx.m[last % kMail], lane, rs, rc, pre);
+          handle(a, T, x * (a.share_ranges) + 4 * reg + slot, bx.m[last % kMail], lane, rs, rc, pre, true);
         }
       }
       return;
@@ -1260,7 +1260,7 @@ struct Fast {
   // in tile order (this one straight from LDS), writes the rows and resets
   // the counter to zero.
   static __device__ void handle(const DecodeArgs &a, int64_t T, int64_t rid, const Mail &e, int lane,
-                                const int64_t *rs, const int *rc, Pre &pre) {
+                                const int64_t *rs, const int *rc, Pre &pre, bool probe = false) {
     const int NX = a.num_xcd;
     const int hc = e.hcount;
     const int64_t row0 = e.row0;
@@ -1291,7 +1291,18 @@ struct Fast {
     const auto ro = float_rsrc(a.part_o, NX * sr * 2 * GT * kHd);
     const auto rm = float_rsrc(a.part_m, NX * sr * 2 * kSlotMlFloats);
     const int own = static_cast<int>(rid * 2 + e.side);
-    if (cross) {
+    uint64_t *ctr = unit_ctr(a, e.unit);
+    // `probe` (the range's last segment, taken by the streamer): when every
+    // other holder is counted in already, this one is the last for sure, so
+    // it merges at once and publishes and counts nothing
+    bool last_for_sure = false;
+    if (probe && known) {
+      uint64_t c = 0;
+      if (lane == 0) c = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_for_sure = static_cast<uint64_t>(uniform(static_cast<int64_t>(c))) == static_cast<uint64_t>(count - 1);
+    }
+    if (last_for_sure) {
+    } else if (cross) {
       for (int i = lane; i < GT * (kHd / 4); i += 64) rsrc_store4(ro, (own * (GT * kHd) + 4 * i) * 4, e.o[i]);
       if (lane < GT) rsrc_store2(rm, (own * kSlotMlFloats + 2 * lane) * 4, e.ml[lane]);
     } else {
@@ -1302,11 +1313,12 @@ struct Fast {
       if (lane < GT)
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(w2, e.ml[lane]), rm, (own * kSlotMlFloats + 2 * lane) * 4, 0, 0);
     }
-    __builtin_amdgcn_s_waitcnt(0x0f70);        // vmcnt(0): published before counted
-    uint64_t *ctr = unit_ctr(a, e.unit);
-    uint64_t old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(ctr, uint64_t{1}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (uniform(static_cast<int64_t>(old)) != count - 1) return;
+    if (!last_for_sure) {
+      __builtin_amdgcn_s_waitcnt(0x0f70);      // vmcnt(0): published before counted
+      uint64_t old = 0;
+      if (lane == 0) old = __hip_atomic_fetch_add(ctr, uint64_t{1}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (uniform(static_cast<int64_t>(old)) != count - 1) return;
+    }
 
     // the last count: fold the unit's partials in tile order, eight loads in
     // flight at a time
