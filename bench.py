@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=64,
                     help="sequences of the batch the oracle baseline processes")
+    ap.add_argument("--partitions", default="",
+                    help="with --workload other than llama3-8b: comma-separated partition sizes to time "
+                         "(default: -1, 0 and the batch's own or 256)")
     ap.add_argument("--workload", default="llama3-8b",
                     choices=["llama3-8b", "mha-13b", "prefix-cow", "fp8-long"],
                     help="llama3-8b: the step above (default).  The others time pa_decode alone on the "
@@ -347,6 +350,8 @@ def other_workload(args, pa, W, torch, dev):
     stream = torch.cuda.current_stream()
     kv_bytes = wl.kv_bytes()
     parts = [-1, 0] + ([wl.partition_size] if wl.partition_size > 0 else [256])
+    if args.partitions:
+        parts = [int(x) for x in args.partitions.split(",")]
     for part in parts:
         ws = pa.new_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                               wl.max_blocks_per_seq, wl.block_size, part, device=dev) if part else None

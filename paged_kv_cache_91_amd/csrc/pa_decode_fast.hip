@@ -1378,15 +1378,64 @@ struct Fast {
     if (lane == 0) __hip_atomic_store(ctr, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  static __device__ void run(const DecodeArgs &a) {
+  // Partitions the workgroups of the split take in turn: for each sequence
+  // (in order), each of its units, each of its partitions; a sequence with
+  // no positions or a bad length has one (that writes its rows).
+  static __device__ __forceinline__ int64_t seq_parts(int n, int maxn, int P) {
+    return (n <= 0 || n > maxn) ? 1 : (n + P - 1) / P;
+  }
+
+  // The split with fixed partitions: gridDim.x workgroups take the batch's
+  // partitions i = blockIdx.x, blockIdx.x + gridDim.x, ... so that the grid
+  // holds no workgroup for a partition past a context's end.
+  static __device__ void run_split(const DecodeArgs &a) {
+    const int lane = threadIdx.x & 63;
+    const int S = a.num_seqs;
+    const int KVG = a.num_kv_heads * a.head_groups;
+    const int maxn = a.max_blocks * BS;
+    const int P = a.partition_size;
+    int64_t base = 0;                  // items before sequence chunk c0
+    int c0 = 0;
+    int64_t incl = 0, cnt = 0;         // this lane's sequence c0 + lane: items up to and including it, its items
+    auto scan = [&]() {
+      const int s = c0 + lane;
+      cnt = s < S ? seq_parts(load_const(a.ctx, s), maxn, P) * KVG : 0;
+      incl = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int64_t up = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += up;
+      }
+    };
+    scan();
+    for (int64_t i = blockIdx.x;; i += gridDim.x) {
+      // advance to the chunk of 64 sequences holding item i (items only grow)
+      while (c0 < S && base + lane_value(incl, 63) <= i) {
+        base += lane_value(incl, 63);
+        c0 += 64;
+        if (c0 < S) scan();
+      }
+      if (c0 >= S) break;
+      const int first = uniform(static_cast<int>(__builtin_ctzll(__builtin_amdgcn_ballot_w64(base + incl > i))));
+      const int seq = c0 + first;
+      const int64_t r = i - (base + lane_value(incl, first) - lane_value(cnt, first));
+      const int64_t np = lane_value(cnt, first) / KVG;
+      const int y = static_cast<int>(r / np);
+      run_item(a, static_cast<int>(r - y * np), y, seq);
+    }
+  }
+
+  static __device__ void run(const DecodeArgs &a) { run_item(a, 0, blockIdx.y, blockIdx.z); }
+
+  // Partition `part` of unit `y` (KV head * head_groups + head group) of
+  // sequence `seq`.
+  static __device__ void run_item(const DecodeArgs &a, int part, int y, int seq) {
     __shared__ float s_ml[NW][GT][2];
     __shared__ float4 s_acc[NW][GT][kHd / 4];
     __shared__ int s_last;
 
-    const int part = blockIdx.x;
-    const int kvh = blockIdx.y / a.head_groups;
-    const int hg = blockIdx.y - kvh * a.head_groups;
-    const int seq = blockIdx.z;
+    const int kvh = y / a.head_groups;
+    const int hg = y - kvh * a.head_groups;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);    // uniform: keeps tile math scalar
     const int lane = tid & 63;
@@ -1471,7 +1520,7 @@ struct Fast {
 
     // split: publish this partition's partial with device-coherent stores,
     // wait until they are complete, then count the arrival
-    const int64_t unit = static_cast<int64_t>(seq) * (a.num_kv_heads * a.head_groups) + blockIdx.y;
+    const int64_t unit = static_cast<int64_t>(seq) * (a.num_kv_heads * a.head_groups) + y;
     float *po = a.part_o + (unit * a.max_parts + part) * (GT * kHd);
     float *pml = a.part_m + (unit * a.max_parts + part) * (GT * 2);
     for (int i = tid; i < GT * (kHd / 4); i += kThreads) {
@@ -1548,6 +1597,14 @@ __global__ __launch_bounds__(NW * 64) void decode_fast_kernel(DecodeArgs a) {
 }
 
 template <typename QS, typename KS, int GT, int BS>
+__global__ __launch_bounds__(kSplitWaves * 64) void decode_split_kernel(DecodeArgs a) {
+  Fast<QS, KS, GT, BS, kSplitWaves>::run_split(a);
+}
+
+// workgroups of the fixed-partition split per compute unit (one wave each)
+constexpr int kSplitWgsPerCu = 32;
+
+template <typename QS, typename KS, int GT, int BS>
 // The fields the launch's first loads depend on come as separate scalar
 // arguments ahead of the struct, so that they can arrive preloaded in SGPRs
 // (kernel-argument preloading) instead of through a load of the argument
@@ -1607,9 +1664,11 @@ hipError_t launch_fast_bs(const DecodeArgs &a, hipStream_t s, const LaunchEvents
     hipExtLaunchKernelGGL(zero_counters_kernel, dim3(static_cast<unsigned>((units + 255) / 256)), dim3(256), 0, s,
                           ev.start, nullptr, 0, a.counters, units);
     const dim3 block(kSplitWaves * 64);
+    const int64_t most = units * a.max_parts;
+    const dim3 sgrid(static_cast<unsigned>(min(most, static_cast<int64_t>(device_compute_units()) * kSplitWgsPerCu)));
     switch (a.heads_per_wg) {
 #define PA_SPLIT(G) \
-      case G: hipExtLaunchKernelGGL((decode_fast_kernel<QS, KS, G, BS, kSplitWaves>), grid, block, 0, s, nullptr, ev.stop, 0, a); break;
+      case G: hipExtLaunchKernelGGL((decode_split_kernel<QS, KS, G, BS>), sgrid, block, 0, s, nullptr, ev.stop, 0, a); break;
       PA_SPLIT(1) PA_SPLIT(2) PA_SPLIT(4) PA_SPLIT(8)
 #undef PA_SPLIT
       default: return hipErrorInvalidValue;
