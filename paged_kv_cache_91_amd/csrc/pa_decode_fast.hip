@@ -1432,7 +1432,6 @@ struct Fast {
   static __device__ void run_item(const DecodeArgs &a, int part, int y, int seq) {
     __shared__ float s_ml[NW][GT][2];
     __shared__ float4 s_acc[NW][GT][kHd / 4];
-    __shared__ int s_last;
 
     const int kvh = y / a.head_groups;
     const int hg = y - kvh * a.head_groups;
@@ -1518,8 +1517,8 @@ struct Fast {
       return;
     }
 
-    // split: publish this partition's partial with device-coherent stores,
-    // wait until they are complete, then count the arrival
+    // split: publish this partition's partial; the merge is a launch of its
+    // own (run_merge), which sees it once this launch has ended
     const int64_t unit = static_cast<int64_t>(seq) * (a.num_kv_heads * a.head_groups) + y;
     float *po = a.part_o + (unit * a.max_parts + part) * (GT * kHd);
     float *pml = a.part_m + (unit * a.max_parts + part) * (GT * 2);
@@ -1529,50 +1528,52 @@ struct Fast {
       float4 o;
       wave_merge(h, d4, big_m, l, o);
       const float mul = any_bad ? nanv : 1.0f;
-      coherent_store4(po + h * kHd + 4 * d4, f32x4_t{o.x * mul, o.y * mul, o.z * mul, o.w * mul});
-      if (d4 == 0) {
-        coherent_store(pml + 2 * h, any_bad ? nanv : big_m);
-        coherent_store(pml + 2 * h + 1, any_bad ? nanv : l);
-      }
+      *reinterpret_cast<float4 *>(po + h * kHd + 4 * d4) = make_float4(o.x * mul, o.y * mul, o.z * mul, o.w * mul);
+      if (d4 == 0) *reinterpret_cast<float2 *>(pml + 2 * h) = make_float2(any_bad ? nanv : big_m, any_bad ? nanv : l);
     }
-    __builtin_amdgcn_s_waitcnt(0x0f70);          // vmcnt(0): this thread's stores have landed
-    __syncthreads();                             // ... and every other thread's
-    if (tid == 0)
-      s_last = __hip_atomic_fetch_add(a.counters + unit, 1, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT) == nparts - 1;
-    __syncthreads();
-    if (!s_last) return;
+  }
 
-    // merge every partition of this (sequence, head group) in partition
-    // order, eight partitions' loads in flight at a time
-    const float *bo = a.part_o + unit * a.max_parts * (GT * kHd);
-    const float *bml = a.part_m + unit * a.max_parts * (GT * 2);
-    for (int i = tid; i < hcount * (kHd / 4); i += kThreads) {
-      const int h = i >> 5, d4 = i & 31;
-      float big_m = -INFINITY, l = 0.0f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      bool nan_seen = false;
-      for (int p0 = 0; p0 < nparts; p0 += 8) {
-        Partial x[8];
+  // The split's merge: workgroup (unit, j) of 64 lanes folds the partials of
+  // query heads 2j and 2j + 1 of that (sequence, head group) in increasing
+  // partition order (lanes 0-31 and 32-63, four dimensions a lane), eight
+  // partitions' loads in flight at a time.  Sequences held by one partition
+  // were written out by the partition itself.
+  static __device__ void run_merge(const DecodeArgs &a) {
+    const int64_t unit = blockIdx.x;
+    const int KVG = a.num_kv_heads * a.head_groups;
+    const int seq = static_cast<int>(unit / KVG);
+    const int y = static_cast<int>(unit - static_cast<int64_t>(seq) * KVG);
+    const int kvh = y / a.head_groups;
+    const int hg = y - kvh * a.head_groups;
+    const int n = load_const(a.ctx, seq);
+    if (n <= 0 || n > a.max_blocks * BS) return;
+    const int P = a.partition_size;
+    const int nparts = (n + P - 1) / P;
+    if (nparts <= 1) return;
+    const int h = 2 * static_cast<int>(blockIdx.y) + (threadIdx.x >> 5);
+    const int hcount = min(GT, a.group - hg * GT);
+    if (h >= hcount) return;
+    const int d4 = threadIdx.x & 31;
+    const int64_t row0 = static_cast<int64_t>(seq) * a.num_q_heads + kvh * a.group + hg * GT;
+    const float *bo = a.part_o + unit * a.max_parts * (GT * kHd) + h * kHd + 4 * d4;
+    const float *bml = a.part_m + unit * a.max_parts * (GT * 2) + 2 * h;
+    float big_m = -INFINITY, l = 0.0f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    bool nan_seen = false;
+    for (int p0 = 0; p0 < nparts; p0 += 8) {
+      Partial x[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int pp = min(p0 + k, nparts - 1);
-          x[k].ml = coherent_load2(bml + pp * GT * 2 + 2 * h);
-          x[k].o0 = coherent_load4(bo + pp * GT * kHd + h * kHd + 4 * d4);
-          x[k].o1 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          coherent_wait(x[k].ml);
-          coherent_wait(x[k].o0);
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (p0 + k < nparts) fold(x[k], big_m, l, o, nan_seen);
+      for (int k = 0; k < 8; ++k) {
+        const int pp = min(p0 + k, nparts - 1);
+        x[k].ml = *reinterpret_cast<const f32x2_t *>(bml + pp * GT * 2);
+        x[k].o0 = *reinterpret_cast<const f32x4_t *>(bo + pp * GT * kHd);
+        x[k].o1 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       }
-      store4(a, (row0 + h) * kHd + 4 * d4, make_float4(o[0], o[1], o[2], o[3]),
-             nan_seen ? nanv : a.v_scale / l);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (p0 + k < nparts) fold(x[k], big_m, l, o, nan_seen);
     }
-    if (tid == 0) __hip_atomic_store(a.counters + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    store4(a, (row0 + h) * kHd + 4 * d4, make_float4(o[0], o[1], o[2], o[3]),
+           nan_seen ? __builtin_nanf("") : a.v_scale / l);
   }
 };
 
@@ -1582,15 +1583,6 @@ struct Fast {
 constexpr int kFastWaves = 4;
 constexpr int kSplitWaves = 1;
 
-// Zeroes the split's arrival counters of this call's (sequence, head group)
-// units before the decode launch, so that a workspace whose bytes earlier
-// calls used for other things (partials of a larger batch) still starts the
-// count at zero.  A kernel rather than a memset keeps the call capturable.
-__global__ __launch_bounds__(256) void zero_counters_kernel(int32_t *c, int64_t n) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i < n) c[i] = 0;
-}
-
 template <typename QS, typename KS, int GT, int BS, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_fast_kernel(DecodeArgs a) {
   Fast<QS, KS, GT, BS, NW>::run(a);
@@ -1599,6 +1591,11 @@ __global__ __launch_bounds__(NW * 64) void decode_fast_kernel(DecodeArgs a) {
 template <typename QS, typename KS, int GT, int BS>
 __global__ __launch_bounds__(kSplitWaves * 64) void decode_split_kernel(DecodeArgs a) {
   Fast<QS, KS, GT, BS, kSplitWaves>::run_split(a);
+}
+
+template <typename QS, typename KS, int GT, int BS>
+__global__ __launch_bounds__(64) void merge_parts_kernel(DecodeArgs a) {
+  Fast<QS, KS, GT, BS, kSplitWaves>::run_merge(a);
 }
 
 // workgroups of the fixed-partition split per compute unit (one wave each)
@@ -1661,14 +1658,16 @@ hipError_t launch_fast_bs(const DecodeArgs &a, hipStream_t s, const LaunchEvents
   const dim3 grid(a.partition_size > 0 ? a.max_parts : 1, a.num_kv_heads * a.head_groups, a.num_seqs);
   if (a.partition_size > 0) {
     const int64_t units = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * a.head_groups;
-    hipExtLaunchKernelGGL(zero_counters_kernel, dim3(static_cast<unsigned>((units + 255) / 256)), dim3(256), 0, s,
-                          ev.start, nullptr, 0, a.counters, units);
     const dim3 block(kSplitWaves * 64);
     const int64_t most = units * a.max_parts;
     const dim3 sgrid(static_cast<unsigned>(min(most, static_cast<int64_t>(device_compute_units()) * kSplitWgsPerCu)));
+    const dim3 mgrid(static_cast<unsigned>(units), static_cast<unsigned>((a.heads_per_wg + 1) / 2));
     switch (a.heads_per_wg) {
 #define PA_SPLIT(G) \
-      case G: hipExtLaunchKernelGGL((decode_split_kernel<QS, KS, G, BS>), sgrid, block, 0, s, nullptr, ev.stop, 0, a); break;
+      case G: \
+        hipExtLaunchKernelGGL((decode_split_kernel<QS, KS, G, BS>), sgrid, block, 0, s, ev.start, nullptr, 0, a); \
+        hipExtLaunchKernelGGL((merge_parts_kernel<QS, KS, G, BS>), mgrid, dim3(64), 0, s, nullptr, ev.stop, 0, a); \
+        break;
       PA_SPLIT(1) PA_SPLIT(2) PA_SPLIT(4) PA_SPLIT(8)
 #undef PA_SPLIT
       default: return hipErrorInvalidValue;
