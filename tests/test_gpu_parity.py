@@ -422,6 +422,43 @@ def test_workspace_reused_across_batches(part):
         assert int(ws.view(torch.int32)[32 * 17].item()) == 0  # never marked
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_fixed_split_never_reads_stale_partials(d):
+    """Fixed partitions with every byte of the workspace past its counters
+    set to NaN beforehand (the counters zero, as the workspace contract asks):
+    a call merges only the partials it has written itself, so the result
+    matches the oracle and, bit for bit, the same call on clean scratch.
+    d 128 runs the head-dim-128 split and its merge launch, d 64 the generic
+    kernels."""
+    rng = np.random.default_rng(71 + d)
+    bs = 16
+    lens = np.concatenate([[1, bs, bs + 1, 200], rng.integers(1, 400, size=5)])
+    need = sum(-(-int(n) // bs) for n in lens)
+    wl = W.build_decode(71 + d, name=f"stale-{d}", q_dtype="bf16", kv_dtype="bf16", num_q_heads=8,
+                        num_kv_heads=2, head_dim=d, block_size=bs, num_blocks=need + 5,
+                        context_lens=lens, rng=rng)
+    dev = DeviceWorkload(wl)
+    ref = oracle_out(wl)
+    units = wl.num_seqs * wl.num_kv_heads          # group 4: one head group per KV head
+    counter_bytes = -(-(units * 8) // 256) * 256
+    for part in (bs, 64):
+        size = pa.pa_decode_workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, d,
+                                            wl.max_blocks_per_seq, bs, part)
+        say(f"[stale partials] d={d} partition {part} workspace {size} B")
+        clean = torch.zeros(size, dtype=torch.uint8, device=DEV)
+        stale = torch.full((size,), 0xFF, dtype=torch.uint8, device=DEV)
+        stale[:counter_bytes] = 0
+        outs = []
+        for ws in (clean, stale):
+            out = torch.full_like(dev.q, float("nan"))
+            got = out_f64(pa.pa_decode(dev.q, dev.pool, dev.tables, dev.ctx, wl.scale, out=out,
+                                       partition_size=part, workspace=ws, q_dtype=wl.q_dtype))
+            assert np.isfinite(got).all(), part
+            assert max_err(got, ref) <= 2e-2, part
+            outs.append(got)
+        assert np.array_equal(outs[0], outs[1]), part
+
+
 @pytest.mark.parametrize("part", [pa.PA_PARTITION_AUTO, 0, 64])
 def test_timed_decode_records_its_kernels(part):
     """pa_time_next_decode: the event pair brackets the call's kernels (a
