@@ -93,9 +93,10 @@ int heads_per_wg(int group) {
 }
 
 // Split-KV scratch.
-//  Fixed partitions: one 8-byte arrival counter per (sequence, head group),
-//  padded to 256 bytes, then float32 partials (m, l and head_dim outputs) for
-//  every (sequence, head group, partition, head of the group).
+//  Fixed partitions: one 8-byte counter per (sequence, head group), padded to
+//  256 bytes (kept zero; the head-dim-128 split merges in a second launch and
+//  does not count arrivals), then float32 partials (m, l and head_dim outputs)
+//  for every (sequence, head group, partition, head of the group).
 //  Balanced split: 4 KiB of registration and exit counters, one 128-byte
 //  counter line per (sequence, head group), then two partial slots per range
 //  of every share (one share per XCD, one range per streaming wave).

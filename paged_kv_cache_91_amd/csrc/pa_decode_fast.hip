@@ -298,7 +298,7 @@ __device__ __forceinline__ int load_const(const int32_t *p, int64_t i) {
 
 // NW waves share one partition: wave w takes tiles w, w+NW, w+2NW, ...; the
 // waves' softmax states are merged through LDS, so a partition costs one
-// partial write and one arrival however many waves stream it.
+// partial write however many waves stream it.
 template <typename QS, typename KS, int GT, int BS, int NW>
 struct Fast {
   using M = Mma<QS>;
