@@ -14,7 +14,11 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libpa.so")
-SOURCES = [os.path.join(PKG, "csrc", f) for f in ("pa_kernels.hip", "pa_decode_fast.hip", "pa_api.cpp")]
+# (source, extra defines) per object; the head-dim-128 decode file is built
+# once per (q, cache) dtype pair so the pairs compile in parallel
+UNITS = [("pa_kernels.hip", []), ("pa_api.cpp", [])] + [
+    ("pa_decode_fast.hip", [f"-DPA_FAST_COMBO={i}"]) for i in range(4)]
+SOURCES = sorted({os.path.join(PKG, "csrc", f) for f, _ in UNITS})
 ARCH = "gfx950"
 
 FLAGS = [
@@ -22,7 +26,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     "-Wno-unused-function",
     # keep packed-fp32 instructions out of the device code
@@ -43,19 +46,36 @@ def hipcc() -> str:
     return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into ``libpa.so``; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, *SOURCES, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with status {res.returncode}")
-    noise = [l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip()]
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+
+
+def _finish(proc, verbose):
+    out, err = proc.communicate()
+    if proc.returncode != 0:
+        sys.stderr.write(out + err)
+        raise RuntimeError(f"hipcc failed with status {proc.returncode}")
+    noise = [l for l in err.splitlines() if "packed-fp32-ops" not in l and l.strip()]
     if verbose and noise:
         sys.stderr.write("\n".join(noise) + "\n")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source (in parallel, one object each) and link
+    ``libpa.so``; returns its path."""
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs, procs = [], []
+    for name, defs in UNITS:
+        obj = os.path.join(objdir, name + "".join(d.replace("-D", ".").replace("=", "") for d in defs) + ".o")
+        objs.append(obj)
+        procs.append(_run([hipcc(), *FLAGS, *defs, "-c", os.path.join(PKG, "csrc", name), "-o", obj], verbose))
+    for p in procs:
+        _finish(p, verbose)
+    tmp = LIB + ".tmp"
+    _finish(_run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose), verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -1692,19 +1692,26 @@ hipError_t launch_fast_t(const DecodeArgs &a, hipStream_t s, const LaunchEvents 
 
 }  // namespace
 
-bool fast_decode_applies(int q_dtype, int kv_dtype, const DecodeArgs &a) {
-  if (a.head_dim != kHd || (a.block_size != 16 && a.block_size != 32)) return false;
-  if (q_dtype != kBF16 && q_dtype != kF16) return false;
-  return kv_dtype == q_dtype || kv_dtype == kFP8;
+// This file is compiled once per (q, cache) dtype pair, PA_FAST_COMBO naming
+// the pair, so that the four sets of kernels build in parallel.
+#if PA_FAST_COMBO == 0
+hipError_t launch_fast_bf16_bf16(const DecodeArgs &a, hipStream_t s, const LaunchEvents &ev) {
+  return launch_fast_t<BF16S, BF16S>(a, s, ev);
 }
-
-hipError_t launch_decode_fast(int q_dtype, int kv_dtype, const DecodeArgs &a, hipStream_t s,
-                              const LaunchEvents &ev) {
-  if (q_dtype == kBF16 && kv_dtype == kBF16) return launch_fast_t<BF16S, BF16S>(a, s, ev);
-  if (q_dtype == kF16 && kv_dtype == kF16) return launch_fast_t<F16S, F16S>(a, s, ev);
-  if (q_dtype == kBF16 && kv_dtype == kFP8) return launch_fast_t<BF16S, FP8S>(a, s, ev);
-  if (q_dtype == kF16 && kv_dtype == kFP8) return launch_fast_t<F16S, FP8S>(a, s, ev);
-  return hipErrorInvalidValue;
+#elif PA_FAST_COMBO == 1
+hipError_t launch_fast_f16_f16(const DecodeArgs &a, hipStream_t s, const LaunchEvents &ev) {
+  return launch_fast_t<F16S, F16S>(a, s, ev);
 }
+#elif PA_FAST_COMBO == 2
+hipError_t launch_fast_bf16_fp8(const DecodeArgs &a, hipStream_t s, const LaunchEvents &ev) {
+  return launch_fast_t<BF16S, FP8S>(a, s, ev);
+}
+#elif PA_FAST_COMBO == 3
+hipError_t launch_fast_f16_fp8(const DecodeArgs &a, hipStream_t s, const LaunchEvents &ev) {
+  return launch_fast_t<F16S, FP8S>(a, s, ev);
+}
+#else
+#error "PA_FAST_COMBO must name a dtype pair (0..3)"
+#endif
 
 }  // namespace pa_impl

@@ -74,17 +74,30 @@ hipError_t launch_write(int src_dtype, int dst_dtype, const WriteArgs &a, hipStr
                         bool *supported);
 hipError_t launch_copy(const CopyArgs &a, hipStream_t s);
 
-// head_dim 128 decode with matrix-core q.K^T and the fused split merge
-// (pa_decode_fast.hip); fast_decode_applies() says whether it covers a call.
-bool fast_decode_applies(int q_dtype, int kv_dtype, const DecodeArgs &a);
 // Events the launch records as its first kernel begins and its last kernel
 // ends (none when null).
 struct LaunchEvents {
   hipEvent_t start = nullptr;
   hipEvent_t stop = nullptr;
 };
-hipError_t launch_decode_fast(int q_dtype, int kv_dtype, const DecodeArgs &a, hipStream_t s,
-                              const LaunchEvents &ev);
+// one launcher per (q, cache) dtype pair (each built from pa_decode_fast.hip)
+hipError_t launch_fast_bf16_bf16(const DecodeArgs &a, hipStream_t s, const LaunchEvents &ev);
+hipError_t launch_fast_f16_f16(const DecodeArgs &a, hipStream_t s, const LaunchEvents &ev);
+hipError_t launch_fast_bf16_fp8(const DecodeArgs &a, hipStream_t s, const LaunchEvents &ev);
+hipError_t launch_fast_f16_fp8(const DecodeArgs &a, hipStream_t s, const LaunchEvents &ev);
+inline bool fast_decode_applies(int q_dtype, int kv_dtype, const DecodeArgs &a) {
+  if (a.head_dim != 128 || (a.block_size != 16 && a.block_size != 32)) return false;
+  if (q_dtype != kBF16 && q_dtype != kF16) return false;
+  return kv_dtype == q_dtype || kv_dtype == kFP8;
+}
+inline hipError_t launch_decode_fast(int q_dtype, int kv_dtype, const DecodeArgs &a, hipStream_t s,
+                                     const LaunchEvents &ev) {
+  if (q_dtype == kBF16 && kv_dtype == kBF16) return launch_fast_bf16_bf16(a, s, ev);
+  if (q_dtype == kF16 && kv_dtype == kF16) return launch_fast_f16_f16(a, s, ev);
+  if (q_dtype == kBF16 && kv_dtype == kFP8) return launch_fast_bf16_fp8(a, s, ev);
+  if (q_dtype == kF16 && kv_dtype == kFP8) return launch_fast_f16_fp8(a, s, ev);
+  return hipErrorInvalidValue;
+}
 
 // Compute units of the current device (256 when it cannot be queried, e.g.
 // on a machine without a GPU, where only sizes are computed).
