@@ -22,9 +22,14 @@ Reported (one JSON line):
                the synchronised wall time of the timed steps;
   roofline     the decode kernel alone, timed with the HIP event pair its
                launch records as it begins and ends (pa_time_next_decode):
-               algorithmic bytes per launch / mean event duration, against
-               MI355X's 8 TB/s HBM peak (stream_bracket_mean_us: events
-               recorded on the stream around the whole call, for reference);
+               algorithmic bytes per launch / MEDIAN event duration, against
+               MI355X's 8 TB/s HBM peak (the mean is reported beside it;
+               stream_bracket_mean_us: events recorded on the stream around
+               the whole call, for reference).  `traffic` is the HBM byte
+               count per launch from the committed rocprofv3 counter runs
+               (profiles/decode_traffic.json), reported only while the decode
+               kernel's source hash matches the one they were taken on;
+               `traffic_source` names the file and the counter scale factors;
   cpu_baseline the float64 oracle (write + decode) on the same batch, on this
                host's cores (skipped with --no-cpu-baseline).
 """
@@ -78,10 +83,11 @@ def log(msg):
 DECODE_SOURCES = ("pa_decode_fast.hip", "pa_common.h", "pa_internal.h")
 
 
-def measured_traffic(partition):
-    """HBM bytes per decode launch from the committed rocprofv3 counter runs,
-    or None when the decode kernel's source (or the partition size) differs
-    from the one the counters were taken on."""
+def recorded_traffic(partition):
+    """HBM bytes per decode launch from the committed rocprofv3 counter runs
+    (with the record they come from), or (None, None) when the decode
+    kernel's source (or the partition size) differs from the one the
+    counters were taken on."""
     import hashlib
     try:
         with open(os.path.join(ROOT, "profiles", "decode_traffic.json")) as f:
@@ -91,10 +97,13 @@ def measured_traffic(partition):
             with open(os.path.join(ROOT, "paged_kv_cache_91_amd", "csrc", name), "rb") as f:
                 h.update(f.read())
     except (OSError, ValueError):
-        return None
+        return None, None
     if rec.get("kernel_source_sha256") != h.hexdigest() or rec.get("partition_size") != partition:
-        return None
-    return rec.get("hbm_bytes_per_launch")
+        return None, None
+    src = {"kind": "recorded, not measured in this run", "file": "profiles/decode_traffic.json"}
+    src.update({k: rec[k] for k in ("fetch_kib_per_launch", "write_kib_per_launch", "fetch_scale",
+                                    "write_scale", "calibration") if k in rec})
+    return rec.get("hbm_bytes_per_launch"), src
 
 
 def main():
@@ -175,10 +184,13 @@ def main():
         if ev is not None:
             ev[1].record(stream)
 
-    for k in range(args.warmup):
+    # at least one warmup step per rotated layer, so every pool has been
+    # touched before the timed region
+    warmup_run = max(args.warmup, args.layers)
+    for k in range(warmup_run):
         step(k)
     torch.cuda.synchronize()
-    log(f"[bench] warmup {args.warmup} steps done")
+    log(f"[bench] warmup {warmup_run} steps done")
 
     # timed region 1 (the value): K steps, each decode call bracketed by a
     # pair of events on the stream
@@ -213,9 +225,9 @@ def main():
     value = kv_bytes * args.steps / elapsed / 1e9
     dec_mean = statistics.fmean(decode_ms)
     dec_med = statistics.median(decode_ms)
-    achieved = kv_bytes / (dec_mean * 1e-3) / 1e9
+    achieved = kv_bytes / (dec_med * 1e-3) / 1e9
+    traffic, traffic_src = recorded_traffic(args.partition)
 
-    # parity spot check of the last timed output against the first layer's oracle
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -223,6 +235,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warmup_run,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -247,8 +260,11 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.partition),
-            "timing": "HIP events recorded by the decode kernel's launch as it begins and ends",
+            "traffic": traffic,
+            "traffic_source": traffic_src,
+            "timing": "HIP events recorded by the decode kernel's launch as it begins and ends; "
+                      "achieved uses the median",
+            "achieved_at_mean": round(kv_bytes / (dec_mean * 1e-3) / 1e9, 2),
             "mean_us": round(dec_mean * 1e3, 2),
             "median_us": round(dec_med * 1e3, 2),
             "p10_us": round(sorted(decode_ms)[len(decode_ms) // 10] * 1e3, 2),

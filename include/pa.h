@@ -212,6 +212,43 @@ int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
 int pa_copy_blocks(const pa_kv_pool *pool, const int64_t *src_dst_pairs, int32_t num_pairs,
                    pa_stream_t stream);
 
+/*
+ * pa_decode_status -- health of a workspace the balanced split
+ * (PA_PARTITION_AUTO) has used.  Enqueues on `stream` a one-thread kernel
+ * that writes the workspace's status word to *status:
+ *   PA_WS_CLEAN      (0)  every call so far found its counters in order;
+ *   PA_WS_MISPLACED  (1)  a launch found the workgroups dealt to the XCDs
+ *                         otherwise than in turn (its rows were written NaN);
+ *   PA_WS_TIMED_OUT  (2)  a wait between the waves of one workgroup passed
+ *                         its poll bound, which the protocol never needs (a
+ *                         fault; the launch wrote NaN rows and every wave
+ *                         exited normally).
+ * A workspace whose status is not PA_WS_CLEAN makes every later call write
+ * NaN rows until it is zero-filled.  The value is ready once `stream` has
+ * reached this point (synchronise, or order later work after it).
+ *
+ *   workspace, workspace_bytes  the workspace given to pa_decode (>= 4096
+ *                 bytes when partition_size is PA_PARTITION_AUTO).
+ *   partition_size  the mode the workspace serves; any mode other than
+ *                 PA_PARTITION_AUTO keeps no status and gives PA_WS_CLEAN.
+ *   status        device memory, or host memory from hipHostMalloc, 4 bytes.
+ */
+#define PA_WS_CLEAN 0
+#define PA_WS_MISPLACED 1
+#define PA_WS_TIMED_OUT 2
+int pa_decode_status(const void *workspace, size_t workspace_bytes, int32_t partition_size,
+                     int32_t *status, pa_stream_t stream);
+
+/*
+ * pa_set_wait_polls -- test hook.  Sets, for the calling thread's later
+ * pa_decode calls, how many polls a wait between the waves of one
+ * balanced-split workgroup makes before it gives up (see PA_WS_TIMED_OUT);
+ * 0 restores the default (2^20 polls, tens of milliseconds).  A small value
+ * lets a test force the give-up path from the host while every wave still
+ * exits normally.  Returns PA_ERR_INVALID_ARG for a negative value.
+ */
+int pa_set_wait_polls(int32_t polls);
+
 /* Static text for a pa_status value. */
 const char *pa_status_string(int status);
 

@@ -169,8 +169,22 @@ class BlockAllocator:
         must apply (``pa_copy_blocks``) before writing them: a token that
         lands in a partly filled last block that other tables share triggers
         a copy of that block to a fresh one.
+
+        The call is all or nothing: the fresh blocks it needs (one per block
+        boundary crossed, plus one for a copy-on-write of a shared partly
+        filled last block, which can only concern the first new token) are
+        counted first, and OutOfBlocks is raised before anything changes.
         """
+        if count < 0:
+            raise AllocatorError("count must be >= 0")
         table = self._tables[seq_id]
+        start = self._lengths[seq_id]
+        fresh = -(-(start + count) // self.block_size) - -(-start // self.block_size)
+        cow = count > 0 and start % self.block_size != 0 and \
+            self._refcount[table[start // self.block_size]] > 1
+        if fresh + int(cow) > len(self._free):
+            raise OutOfBlocks(f"append of {count} tokens needs {fresh + int(cow)} blocks, "
+                              f"{len(self._free)} free")
         pairs: List[Tuple[int, int]] = []
         slots = np.empty(count, dtype=np.int64)
         for i in range(count):

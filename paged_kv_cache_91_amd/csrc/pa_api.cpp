@@ -20,6 +20,8 @@ namespace {
 thread_local char g_last_error[256] = "";
 // the event pair pa_time_next_decode set for this thread's next pa_decode
 thread_local pa_impl::LaunchEvents g_next_events;
+// the poll bound of the balanced split's waits for this thread's calls
+thread_local int32_t g_wait_polls = pa_impl::kDefaultWaitPolls;
 
 int fail(int status, const char *fmt, ...) {
   va_list ap;
@@ -259,6 +261,7 @@ int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
   const double ks = pool->dtype == PA_FP8_E4M3 ? static_cast<double>(pool->k_scale) : 1.0;
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * ks * log2e);
   a.v_scale = pool->dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
+  a.wait_polls = g_wait_polls;
 
   const bool fast = pa_impl::fast_decode_applies(q_dtype, pool->dtype, a);
   if (partition_size == PA_PARTITION_AUTO && !fast) {
@@ -324,6 +327,28 @@ int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
     if (e == hipSuccess && ev.stop) e = hipEventRecord(ev.stop, hs);
   }
   if (e != hipSuccess) return hip_fail(e);
+  return ok();
+}
+
+int pa_decode_status(const void *workspace, size_t workspace_bytes, int32_t partition_size,
+                     int32_t *status, pa_stream_t stream) {
+  if (!status) return fail(PA_ERR_INVALID_ARG, "status is NULL");
+  if (partition_size < 0 && partition_size != PA_PARTITION_AUTO)
+    return fail(PA_ERR_INVALID_ARG, "partition_size must be >= 0 or PA_PARTITION_AUTO");
+  const int32_t *word = nullptr;
+  if (partition_size == PA_PARTITION_AUTO) {
+    if (!workspace || workspace_bytes < 4096)
+      return fail(PA_ERR_WORKSPACE, "a balanced-split workspace holds at least 4096 bytes");
+    word = reinterpret_cast<const int32_t *>(static_cast<const char *>(workspace) + pa_impl::kWsStatusOffset);
+  }
+  hipError_t e = pa_impl::launch_status(word, status, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return ok();
+}
+
+int pa_set_wait_polls(int32_t polls) {
+  if (polls < 0) return fail(PA_ERR_INVALID_ARG, "polls must be >= 0");
+  g_wait_polls = polls == 0 ? pa_impl::kDefaultWaitPolls : polls;
   return ok();
 }
 

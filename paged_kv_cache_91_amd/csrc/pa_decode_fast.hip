@@ -844,6 +844,9 @@ struct Fast {
   // counters at a.counters + 32 * unit (one 128-byte line each, 64-bit).
   static __device__ __forceinline__ int *reg_ctr(const DecodeArgs &a, int64_t x) { return a.ctl + 32 * (x + 1); }
   static __device__ __forceinline__ int *poison_word(const DecodeArgs &a) { return a.ctl + 32 * 17; }
+  // values of the poison word (the status pa_decode_status reads back)
+  static constexpr int kWsMisplaced = 1;   // the grid was not dealt to the XCDs in turn
+  static constexpr int kWsTimedOut = 2;    // a wait between waves of a workgroup ran out
 
   // NaN into output rows first, first + step, ... of the batch
   static __device__ void nan_rows(const DecodeArgs &a, int64_t first, int64_t step, int lane) {
@@ -854,6 +857,28 @@ struct Fast {
   }
   static __device__ __forceinline__ uint64_t *unit_ctr(const DecodeArgs &a, int64_t unit) {
     return reinterpret_cast<uint64_t *>(a.counters) + 16 * unit;
+  }
+
+  // Waits between the waves of one workgroup (all resident together, so
+  // each wait ends as soon as the other wave gets there) are bounded all the
+  // same: after a.wait_polls polls without the condition, the wave gives up.
+  // `ready` reads LDS words other waves write; the result is made uniform.
+  template <typename F>
+  static __device__ __forceinline__ bool wait_lds(F ready, int polls) {
+    for (int i = 0;; ++i) {
+      if (uniform(static_cast<int>(ready())) != 0) return true;
+      if (i >= polls) return false;
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  // A wave whose wait ran out (a protocol fault): it marks the workspace
+  // (read back through pa_decode_status; later calls write NaN rows until the
+  // workspace is zero-filled, since its counters can no longer be trusted)
+  // and writes NaN into every output row, so that no row this launch owed is
+  // left stale; then it exits like every other wave.
+  static __device__ void abandon(const DecodeArgs &a, int lane) {
+    if (lane == 0) __hip_atomic_store(poison_word(a), kWsTimedOut, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    nan_rows(a, 0, 1, lane);
   }
 
   static __device__ void run_pair(const DecodeArgs &a) {
@@ -905,7 +930,7 @@ struct Fast {
       // strided share from each workgroup of a marked one), nothing else
       if (helper) {
         if (reg >= n_x && wave == 4 && lane == 0)
-          __hip_atomic_store(poison_word(a), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(poison_word(a), kWsMisplaced, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (reg >= n_x)
           nan_rows(a, wave - 4, 4, lane);
         else
@@ -932,9 +957,13 @@ struct Fast {
     if (!helper) {
       int64_t lo, hi;
       range_of(sh, 4 * reg + slot, lo, hi);
-      if (lo < hi) stream(a, bx, s_q[slot], lo, hi, lane, n_lane, cnt0, incl0);
+      const bool streamed = lo >= hi || stream(a, bx, s_q[slot], lo, hi, lane, n_lane, cnt0, incl0);
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       if (lane == 0) lds_put(&bx.done, 1);
+      if (!streamed) {
+        abandon(a, lane);
+        return;
+      }
       // the range's last segment, unless the helper already took it: the
       // helper may still be merging the segment before, and this is the
       // merge on the launch's critical path
@@ -947,7 +976,10 @@ struct Fast {
                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
         if (uniform(won) != 0) {
-          while (lds_get(&s_tbl) < 4 || lds_get(&s_preok) < 4) __builtin_amdgcn_s_sleep(1);
+          if (!wait_lds([&] { return lds_get(&s_tbl) >= 4 && lds_get(&s_preok) >= 4; }, a.wait_polls)) {
+            abandon(a, lane);
+            return;
+          }
           __atomic_signal_fence(__ATOMIC_SEQ_CST);
           Pre pre = s_pre[slot];
           handle(a, T, x * (a.share_ranges) + 4 * reg + slot, bx.m[last % kMail], lane, rs, rc, pre, true);
@@ -976,7 +1008,11 @@ struct Fast {
       }
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       if (lane == 0) __hip_atomic_fetch_add(&s_tbl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      while (lds_get(&s_tbl) < 4) __builtin_amdgcn_s_sleep(1);   // the four helpers have filled it
+      // the four helpers have filled it
+      if (!wait_lds([&] { return lds_get(&s_tbl) >= 4; }, a.wait_polls)) {
+        abandon(a, lane);
+        return;
+      }
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
     int64_t lo, hi;
@@ -987,8 +1023,8 @@ struct Fast {
 
   // The streamer's tile range [lo, hi) of the T-tile list.  Finished
   // segments go to the mailbox `bx`; `sq` stages q of the range's first
-  // kQSlots units.
-  static __device__ void stream(const DecodeArgs &a, Box &bx, uint4 (*sq)[GT * 16], int64_t lo, int64_t hi,
+  // kQSlots units.  False if the wait for a free mailbox entry ran out.
+  static __device__ bool stream(const DecodeArgs &a, Box &bx, uint4 (*sq)[GT * 16], int64_t lo, int64_t hi,
                                 int lane, int n_lane, int64_t cnt0, int64_t incl0) {
     const int r16 = lane & 15;
     const int g4 = lane >> 4;
@@ -1115,11 +1151,8 @@ struct Fast {
             // partial for a split unit, handed to the helper
             const float l = xor32_sum(xor16_sum(l_run));
             if (head - tail_seen >= kMail) {
-              for (;;) {
-                tail_seen = lds_get(&bx.tail);
-                if (head - tail_seen < kMail) break;
-                __builtin_amdgcn_s_sleep(1);
-              }
+              if (!wait_lds([&] { return head - (tail_seen = lds_get(&bx.tail)) < kMail; }, a.wait_polls))
+                return false;
               __atomic_signal_fence(__ATOMIC_SEQ_CST);
             }
             Mail &e = bx.m[head % kMail];
@@ -1156,6 +1189,7 @@ struct Fast {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    return true;
   }
 
   // The helper of the streamer with range index `rid` (share * share_ranges
@@ -1209,12 +1243,13 @@ struct Fast {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (lane == 0) __hip_atomic_fetch_add(&s_preok, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 
-    int tail = 0;
+    int tail = 0, idle = 0;
     for (;;) {
-      const int done = lds_get(&bx.done);
-      const int head = lds_get(&bx.head);
+      const int done = uniform(lds_get(&bx.done));
+      const int head = uniform(lds_get(&bx.head));
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       if (tail < head) {
+        idle = 0;
         int won = 0;
         if (lane == 0) {
           int expect = 0;
@@ -1228,6 +1263,10 @@ struct Fast {
         continue;
       }
       if (done) break;
+      if (++idle > a.wait_polls) {     // the streamer neither posts nor finishes
+        abandon(a, lane);
+        return;
+      }
       __builtin_amdgcn_s_sleep(1);
     }
   }
@@ -1314,10 +1353,29 @@ struct Fast {
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(w2, e.ml[lane]), rm, (own * kSlotMlFloats + 2 * lane) * 4, 0, 0);
     }
     if (!last_for_sure) {
+      // Ordering of publish -> count -> merge.  The memory model offers no
+      // scope between a workgroup and the whole device, and an agent-scope
+      // release/acquire pair would write back / invalidate the L2 (measured:
+      // the acquire alone re-reads the partials from HBM, +1.3 us).  The
+      // order is kept by the hardware and pinned for the compiler instead:
+      //  * publish: every partial store has completed (vmcnt(0)) before the
+      //    count-in atomic is issued, so a counter value that includes this
+      //    holder implies its partial sits in the L2 the readers use (the
+      //    share's own L2, or memory for the sc1 stores of a unit that
+      //    crosses a share boundary);
+      //  * merge: the partial loads are issued only after the atomic has
+      //    returned the completing count (they depend on its value through
+      //    the branch below), and a compiler fence keeps the compiler from
+      //    moving any memory access across that point;
+      //  * the merging compute unit's L1 holds no stale copy: no line of a
+      //    slot is loaded before the slot is counted in, once per launch, and
+      //    no two slots share a line (sc1 loads bypass it anyway).
       __builtin_amdgcn_s_waitcnt(0x0f70);      // vmcnt(0): published before counted
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
       uint64_t old = 0;
       if (lane == 0) old = __hip_atomic_fetch_add(ctr, uint64_t{1}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (uniform(static_cast<int64_t>(old)) != count - 1) return;
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
 
     // the last count: fold the unit's partials in tile order, eight loads in

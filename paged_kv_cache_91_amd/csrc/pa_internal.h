@@ -40,7 +40,15 @@ struct DecodeArgs {
   int32_t share_ranges;    // balanced split: ranges per share the partial slots are sized for
   float scale_log2;        // scale * k_scale * log2(e)
   float v_scale;           // 1 unless fp8
+  int32_t wait_polls;      // balanced split: polls before a wait between waves of a workgroup gives up
 };
+
+// Polls (each about 30-80 ns) before a wait between the waves of one
+// workgroup gives up: far beyond any wait the protocol has (a peer wave's
+// handling of one mailbox entry, microseconds).
+constexpr int32_t kDefaultWaitPolls = 1 << 20;
+// Byte offset of the balanced split's status word in its workspace.
+constexpr int64_t kWsStatusOffset = 4 * 32 * 17;
 
 struct WriteArgs {
   const void *k;
@@ -73,6 +81,8 @@ hipError_t launch_decode(int q_dtype, int kv_dtype, const DecodeArgs &a, hipStre
 hipError_t launch_write(int src_dtype, int dst_dtype, const WriteArgs &a, hipStream_t s,
                         bool *supported);
 hipError_t launch_copy(const CopyArgs &a, hipStream_t s);
+// *out = word ? *word : 0, one thread, on stream s
+hipError_t launch_status(const int32_t *word, int32_t *out, hipStream_t s);
 
 // Events the launch records as its first kernel begins and its last kernel
 // ends (none when null).

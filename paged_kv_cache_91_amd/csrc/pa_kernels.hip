@@ -461,6 +461,11 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
       *reinterpret_cast<const uint4 *>(pool + src * a.block_bytes + off);
 }
 
+// the balanced split's workspace status word, copied where the caller asks
+__global__ __launch_bounds__(64) void status_kernel(const int32_t *word, int32_t *out) {
+  if (threadIdx.x == 0) *out = word ? __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -523,6 +528,11 @@ hipError_t launch_write(int src_dtype, int dst_dtype, const WriteArgs &a, hipStr
 hipError_t launch_copy(const CopyArgs &a, hipStream_t s) {
   const dim3 grid(a.num_pairs, 2, static_cast<unsigned>((a.block_bytes + 4095) / 4096));
   hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_status(const int32_t *word, int32_t *out, hipStream_t s) {
+  hipLaunchKernelGGL(status_kernel, dim3(1), dim3(64), 0, s, word, out);
   return hipGetLastError();
 }
 

@@ -30,7 +30,9 @@ _TORCH_STORAGE = {PA_F32: (torch.float32,), PA_F16: (torch.float16,),
 _ELEM = {PA_F32: 4, PA_F16: 2, PA_BF16: 2, PA_FP8_E4M3: 1}
 
 EXPORTED = ("pa_write_kv", "pa_decode", "pa_decode_workspace_bytes", "pa_copy_blocks",
-            "pa_status_string", "pa_last_error", "pa_version", "pa_time_next_decode")
+            "pa_status_string", "pa_last_error", "pa_version", "pa_time_next_decode",
+            "pa_decode_status", "pa_set_wait_polls")
+PA_WS_CLEAN, PA_WS_MISPLACED, PA_WS_TIMED_OUT = 0, 1, 2
 
 
 class PaError(RuntimeError):
@@ -87,6 +89,10 @@ def lib() -> ctypes.CDLL:
         L.pa_version.restype = ctypes.c_int
         L.pa_time_next_decode.argtypes = [vp, vp]
         L.pa_time_next_decode.restype = ctypes.c_int
+        L.pa_decode_status.argtypes = [vp, ctypes.c_size_t, i32, vp, vp]
+        L.pa_decode_status.restype = ctypes.c_int
+        L.pa_set_wait_polls.argtypes = [i32]
+        L.pa_set_wait_polls.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -118,6 +124,15 @@ def _stream(stream) -> Optional[int]:
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
+
+
+def _torch_stream(stream, device) -> torch.cuda.Stream:
+    """The torch stream object for ``stream`` (None: the current stream)."""
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
 
 
 def dtype_code(t: torch.Tensor, dtype: Optional[str] = None) -> int:
@@ -179,8 +194,10 @@ def pa_decode(q: torch.Tensor, pool: KvPool, block_tables: torch.Tensor,
               q_dtype: Optional[str] = None, stream=None) -> torch.Tensor:
     """Paged decode attention; returns ``out`` ([S, Hq, D], q's dtype).
 
-    ``workspace`` (split mode) is allocated zero-filled here when not given;
-    pass one from :func:`new_workspace` to keep allocation out of a timed loop.
+    ``workspace`` (split mode) is allocated zero-filled here when not given,
+    on the stream the kernels run on (so the fill is ordered before them, and
+    the memory is not handed out again before they end); pass one from
+    :func:`new_workspace` to keep allocation out of a timed loop.
     """
     if q.dim() != 3:
         raise ValueError("q must be [num_seqs, num_q_heads, head_dim]")
@@ -195,16 +212,20 @@ def pa_decode(q: torch.Tensor, pool: KvPool, block_tables: torch.Tensor,
         raise ValueError("out must match q in shape and dtype")
     qcode = dtype_code(q, q_dtype)
     maxb = int(block_tables.shape[1])
-    ws_ptr, ws_bytes = None, 0
+    ws_ptr, ws_bytes, own_ws = None, 0, None
     if partition_size != 0:
         if workspace is None:
-            workspace = new_workspace(s, hq, pool.num_kv_heads, d, maxb, pool.block_size,
-                                      partition_size, device=q.device)
+            own_ws = _torch_stream(stream, q.device)
+            with torch.cuda.stream(own_ws):
+                workspace = new_workspace(s, hq, pool.num_kv_heads, d, maxb, pool.block_size,
+                                          partition_size, device=q.device)
         ws_ptr, ws_bytes = _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size()
     _check(lib().pa_decode(_ptr(q, "q"), qcode, s, hq, ctypes.byref(pool), _ptr(block_tables, "block_tables"),
                            maxb, _ptr(context_lens, "context_lens"), float(scale), _ptr(out, "out"),
                            int(partition_size), ws_ptr, ws_bytes, _stream(stream)),
            "pa_decode")
+    if own_ws is not None:
+        workspace.record_stream(own_ws)
     return out
 
 
@@ -226,3 +247,22 @@ def pa_time_next_decode(start, stop) -> None:
         raise ValueError("give both events or neither")
     _check(lib().pa_time_next_decode(None if start is None else start.cuda_event,
                                      None if stop is None else stop.cuda_event), "pa_time_next_decode")
+
+
+def pa_decode_status(workspace: torch.Tensor, partition_size: int, stream=None) -> int:
+    """Status word of a workspace (PA_WS_CLEAN / PA_WS_MISPLACED /
+    PA_WS_TIMED_OUT); waits for ``stream`` to reach the read."""
+    st = _torch_stream(stream, workspace.device)
+    with torch.cuda.stream(st):
+        out = torch.full((1,), -1, dtype=torch.int32, device=workspace.device)
+    _check(lib().pa_decode_status(_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                  int(partition_size), _ptr(out, "status"), _stream(stream)),
+           "pa_decode_status")
+    st.synchronize()
+    return int(out.item())
+
+
+def pa_set_wait_polls(polls: int) -> None:
+    """Test hook: poll bound of the balanced split's in-workgroup waits for
+    this thread's later calls (0 restores the default)."""
+    _check(lib().pa_set_wait_polls(int(polls)), "pa_set_wait_polls")

@@ -147,3 +147,14 @@ def test_time_next_decode_validation():
     assert lib.pa_time_next_decode(FAKE, FAKE * 2) == 0
     assert _decode(_pool(block_size=3)) == -1
     assert _decode(_pool(), num_seqs=0) == 0
+
+
+def test_status_query_and_wait_polls_validation():
+    lib = pa.lib()
+    assert lib.pa_decode_status(FAKE, 8192, -1, None, None) == -1           # no status pointer
+    assert lib.pa_decode_status(FAKE, 8192, -5, FAKE, None) == -1           # bad mode
+    assert lib.pa_decode_status(FAKE, 100, -1, FAKE, None) == -3            # not a balanced-split workspace
+    assert lib.pa_decode_status(None, 8192, -1, FAKE, None) == -3
+    assert lib.pa_set_wait_polls(-1) == -1
+    assert lib.pa_set_wait_polls(5) == 0
+    assert lib.pa_set_wait_polls(0) == 0                                    # back to the default

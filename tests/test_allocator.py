@@ -137,7 +137,14 @@ def test_random_operations_keep_invariants():
                 next_id += 1
             elif op == 1:
                 s = live[rng.integers(len(live))]
-                a.append_tokens(s, int(rng.integers(1, 20)))
+                before = (a.block_table(s), a.length(s), a.free_block_ids(), a.stats())
+                try:
+                    a.append_tokens(s, int(rng.integers(1, 20)))
+                except OutOfBlocks:
+                    # all or nothing: a refused append changes no state
+                    assert (a.block_table(s), a.length(s), a.free_block_ids(), a.stats()) == before
+                    a.check()
+                    raise
             elif op == 2:
                 s = live[rng.integers(len(live))]
                 a.fork(s, next_id)
@@ -150,11 +157,27 @@ def test_random_operations_keep_invariants():
             for s in live:
                 a.free(s)
             live = []
-            # an interrupted append may leave a partly grown table; rebuild
-            a = BlockAllocator(200, 8)
         a.check()
         for s in live:
             n = a.length(s)
             if n:
                 slots = a.slots(s, 0, n)
                 assert len(np.unique(slots)) == n
+
+
+def test_refused_append_changes_nothing():
+    """An append that cannot get every block it needs (here the copy-on-write
+    block for a shared partly filled last block, plus fresh blocks for the
+    tokens after it) raises before any state changes."""
+    a = BlockAllocator(4, 4)
+    a.add_sequence(0, 6)                      # blocks for positions 0..7, last half full
+    a.fork(0, 1)                              # both share both blocks
+    table, pairs_before = a.block_table(1), a.stats().cow_copies
+    with pytest.raises(OutOfBlocks):
+        a.append_tokens(1, 7)                 # needs 1 CoW block + 2 fresh ones; 2 free
+    assert a.block_table(1) == table and a.length(1) == 6
+    assert a.stats().cow_copies == pairs_before and a.num_free == 2
+    a.check()
+    slots, pairs = a.append_tokens(1, 6)      # 1 CoW block + 1 fresh one: fits
+    assert len(pairs) == 1 and len(slots) == 6 and a.num_free == 0
+    a.check()

@@ -103,6 +103,9 @@ SHAPES = [
     ("f32", "f32", 2, 1, 8, 2),
     ("bf16", "bf16", 2, 1, 8, 64),
     ("f32", "f32", 8, 4, 256, 16),
+    ("bf16", "bf16", 16, 8, 128, 16),     # group 2: two heads per head-dim-128 workgroup
+    ("bf16", "bf16", 32, 2, 128, 16),     # group 16: two head groups of 8 per KV head
+    ("f16", "f16", 48, 2, 128, 32),       # group 24: three head groups of 8
 ]
 
 
@@ -342,6 +345,28 @@ def test_nondefault_stream():
     assert max_err(out_f64(out), ref) <= 2e-2
 
 
+@pytest.mark.parametrize("part", [64, pa.PA_PARTITION_AUTO])
+def test_stream_argument_not_current(part):
+    """stream=s without making s current: the workspace the binding allocates
+    is zero-filled on s itself, ahead of the kernels, and held until they end."""
+    wl = W.config2(seed=45, num_seqs=5, ctx_range=(10, 700), num_blocks=256)
+    dev = DeviceWorkload(wl)
+    ref = oracle_out(wl)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(3):
+        out = torch.full_like(dev.q, float("nan"))
+        s.wait_stream(torch.cuda.current_stream())
+        pa.pa_decode(dev.q, dev.pool, dev.tables, dev.ctx, wl.scale, out=out, partition_size=part,
+                     q_dtype=wl.q_dtype, stream=s)
+        s.synchronize()
+        outs.append(out_f64(out))
+    for got in outs:
+        assert max_err(got, ref) <= 2e-2
+        assert np.array_equal(got, outs[0])
+
+
 # ---------------------------------------------------------------------------
 # the balanced split's placement check, forced from the host through the
 # workspace's control words (int32 index 32 * (1 + x): XCD x's registration
@@ -371,6 +396,7 @@ def test_placement_check_marks_workspace_until_zeroed(surplus):
     ref = oracle_out(wl)
     ws = _auto_ws(wl)
     assert max_err(_auto(dev, ws), ref) <= 2e-2
+    assert pa.pa_decode_status(ws, pa.PA_PARTITION_AUTO) == pa.PA_WS_CLEAN
     words = ws.view(torch.int32)
     if surplus == "one_xcd":
         words[32 * 1] = 1 << 20
@@ -385,10 +411,39 @@ def test_placement_check_marks_workspace_until_zeroed(surplus):
     else:
         assert np.isnan(got).all()
     assert int(words[32 * 17].item()) == 1
+    assert pa.pa_decode_status(ws, pa.PA_PARTITION_AUTO) == pa.PA_WS_MISPLACED
     assert np.isnan(_auto(dev, ws)).all()           # marked: every row NaN
     ws.zero_()
     for _ in range(2):
         assert max_err(_auto(dev, ws), ref) <= 2e-2
+    assert pa.pa_decode_status(ws, pa.PA_PARTITION_AUTO) == pa.PA_WS_CLEAN
+
+
+def test_wait_bound_gives_up_marks_and_exits():
+    """The balanced split's waits between the waves of a workgroup are
+    bounded.  With the bound forced down to one poll from the host, waits
+    that would normally last microseconds give up: the launch still ends
+    (every wave exits), the status word says PA_WS_TIMED_OUT, rows are NaN
+    rather than stale, later calls give NaN rows until the workspace is
+    zero-filled, and then the results are exact again."""
+    wl = W.config2(seed=46, num_seqs=8, ctx_range=(300, 1200), num_blocks=700)
+    dev = DeviceWorkload(wl)
+    ref = oracle_out(wl)
+    ws = _auto_ws(wl)
+    say("[wait bound] one poll")
+    pa.pa_set_wait_polls(1)
+    try:
+        got = _auto(dev, ws)
+    finally:
+        pa.pa_set_wait_polls(0)
+    torch.cuda.synchronize()
+    assert pa.pa_decode_status(ws, pa.PA_PARTITION_AUTO) == pa.PA_WS_TIMED_OUT
+    assert np.isnan(got).any()
+    assert np.isnan(_auto(dev, ws)).all()           # marked: every row NaN
+    ws.zero_()
+    assert max_err(_auto(dev, ws), ref) <= 2e-2
+    assert pa.pa_decode_status(ws, pa.PA_PARTITION_AUTO) == pa.PA_WS_CLEAN
+    assert pa.pa_decode_status(ws, 64) == pa.PA_WS_CLEAN      # other modes keep no status
 
 
 @pytest.mark.parametrize("part", [pa.PA_PARTITION_AUTO, 64])
