@@ -922,9 +922,14 @@ struct Fast {
       }
     }
     __syncthreads();
-    const int64_t reg = s_reg;
+    // values read back from LDS are per-lane to the compiler: everything the
+    // tile loop's addresses and trip counts derive from is made uniform, so
+    // that the cursor stays in scalar registers and table entries and lengths
+    // remain scalar loads (a vector load there would wait for every tile
+    // load in flight)
+    const int64_t reg = uniform(static_cast<int64_t>(s_reg));
     const int64_t n_x = wgs_on(x, NX);
-    if (reg >= n_x || s_poison != 0) {
+    if (reg >= n_x || uniform(s_poison) != 0) {
       // a misplaced grid (this workgroup is surplus on its XCD) or a marked
       // workspace: NaN rows (all of them from the surplus workgroup, a
       // strided share from each workgroup of a marked one), nothing else
@@ -1031,6 +1036,8 @@ struct Fast {
     const int KVG = a.num_kv_heads * a.head_groups;
     const int maxn = a.max_blocks * BS;
     const float nanv = __builtin_nanf("");
+    lo = uniform(lo);
+    hi = uniform(hi);
     const Cursor c0 = locate(a, lo, lane, n_lane, cnt0, incl0);
 
     // Set-up order: the first table entry, the q loads, then the first
@@ -1112,6 +1119,7 @@ struct Fast {
     V8 qb[4];
     bool bad = false;
     int head = 0, tail_seen = 0;       // mailbox entries posted / known to be free
+    bool gave_up = false;              // the wait for a free entry ran out: post nothing more
 
     for (int64_t g0 = lo; g0 < hi; g0 += kRing) {
 #pragma unroll
@@ -1150,11 +1158,19 @@ struct Fast {
             // the segment ends: a whole unit's outputs or this range's
             // partial for a split unit, handed to the helper
             const float l = xor32_sum(xor16_sum(l_run));
-            if (head - tail_seen >= kMail) {
-              if (!wait_lds([&] { return head - (tail_seen = lds_get(&bx.tail)) < kMail; }, a.wait_polls))
-                return false;
+            if (head - tail_seen >= kMail && !gave_up) {
+              for (int polls = 0;; ++polls) {
+                tail_seen = uniform(lds_get(&bx.tail));
+                if (head - tail_seen < kMail) break;
+                if (polls >= a.wait_polls) {
+                  gave_up = true;
+                  break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+              }
               __atomic_signal_fence(__ATOMIC_SEQ_CST);
             }
+            if (!gave_up) {
             Mail &e = bx.m[head % kMail];
             const float mul = bad ? nanv : 1.0f;
             if (r16 < GT) {
@@ -1180,6 +1196,7 @@ struct Fast {
             ++head;
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             if (lane == 0) lds_put(&bx.head, head);
+            }
           }
           advance(a, cc, KVG, maxn, n_lane);
           ++gc;
@@ -1189,7 +1206,7 @@ struct Fast {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    return true;
+    return !gave_up;
   }
 
   // The helper of the streamer with range index `rid` (share * share_ranges

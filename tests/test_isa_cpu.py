@@ -1,0 +1,52 @@
+"""Code-generation guard for the balanced-split decode kernel (CPU only).
+
+The streaming wave keeps two K/V tiles (16 loads) in flight while it computes
+the current one.  That depends on the tile loop's cursor staying in scalar
+registers: once the compiler treats it as per-lane, table entries and
+context lengths become vector loads, and each such load waits for every
+tile load issued before it, which cost a third of the kernel's speed once.
+This test compiles the head-dim-128 kernels to gfx950 assembly and checks
+the signature of the intended schedule in decode_pair_kernel<bf16, bf16,
+group 4, block 16>, the kernel the Llama-3-8B-shaped layer runs:
+
+* the first waits inside the tile loop leave 14 loads outstanding;
+* at most a handful of vector dword loads in the whole kernel (set-up and
+  merge only).
+"""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+from paged_kv_cache_91_amd import build as B
+
+KERNEL = "_ZN7pa_impl12_GLOBAL__N_118decode_pair_kernelINS0_5BF16SES2_Li4ELi16EEEvPKiPiiiiiiNS_10DecodeArgsE"
+
+
+@pytest.fixture(scope="module")
+def pair_isa(tmp_path_factory):
+    out = tmp_path_factory.mktemp("isa") / "k.s"
+    cmd = [B.hipcc(), *B.FLAGS, "-DPA_FAST_COMBO=0", "--cuda-device-only", "-S",
+           os.path.join(B.PKG, "csrc", "pa_decode_fast.hip"), "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        pytest.skip("hipcc unavailable: " + res.stderr[-300:])
+    text = out.read_text()
+    start = text.index(KERNEL + ":")
+    end = text.index(".Lfunc_end", start)
+    return text[start:end]
+
+
+def test_tile_loop_keeps_two_tiles_in_flight(pair_isa):
+    lines = pair_isa.splitlines()
+    first_mfma = next(i for i, l in enumerate(lines) if "v_mfma_f32_16x16x32" in l)
+    waits = [int(m.group(1)) for l in lines[first_mfma:first_mfma + 200]
+             for m in [re.search(r"s_waitcnt vmcnt\((\d+)\)", l)] if m]
+    assert waits and max(waits[:3]) >= 12, waits[:8]
+
+
+def test_tile_loop_reads_tables_and_lengths_with_scalar_loads(pair_isa):
+    vector_dword_loads = len(re.findall(r"\bglobal_load_dword\s", pair_isa))
+    assert vector_dword_loads <= 8, vector_dword_loads
