@@ -249,6 +249,32 @@ int pa_decode_status(const void *workspace, size_t workspace_bytes, int32_t part
  */
 int pa_set_wait_polls(int32_t polls);
 
+/*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, meaning, results and errors as
+ * pa_decode, without the workspace: the split-KV scratch is a static device
+ * array inside the library, PA_NOALLOC_SCRATCH_BYTES long, that each GPU the
+ * library runs on holds from the first call on it until the process ends.
+ *
+ * - Calls whose split needs more scratch than that (pa_decode_workspace_bytes
+ *   above PA_NOALLOC_SCRATCH_BYTES) fail with PA_ERR_WORKSPACE and enqueue
+ *   nothing; use pa_decode with a workspace for them.  partition_size 0
+ *   needs no scratch.
+ * - The call allocates and frees nothing.  It enqueues a fill kernel that
+ *   zeroes the scratch's counters ahead of the decode kernels (the scratch
+ *   keeps the last call's contents otherwise), so a call never inherits a
+ *   marked or half-counted state from an earlier one.
+ * - Every call on one GPU shares that GPU's scratch: calls that may overlap
+ *   on one GPU (different streams without ordering, several threads) race
+ *   and give wrong results.  Order them on one stream.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int pa_decode_noalloc(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                      const pa_kv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *context_lens, float scale, void *out, int32_t partition_size,
+                      pa_stream_t stream);
+
 /* Static text for a pa_status value. */
 const char *pa_status_string(int status);
 

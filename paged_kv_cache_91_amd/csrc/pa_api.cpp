@@ -204,6 +204,21 @@ int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
               const pa_kv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
               const int32_t *context_lens, float scale, void *out, int32_t partition_size,
               void *workspace, size_t workspace_bytes, pa_stream_t stream) {
+  return pa_impl::decode_entry(q, q_dtype, num_seqs, num_q_heads, pool, block_tables, max_blocks_per_seq,
+                               context_lens, scale, out, partition_size, workspace, workspace_bytes,
+                               stream, false);
+}
+
+}  // extern "C"
+
+namespace pa_impl {
+
+int set_error(int status, const char *msg) { return fail(status, "%s", msg); }
+
+int decode_entry(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                 const pa_kv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                 const int32_t *context_lens, float scale, void *out, int32_t partition_size,
+                 void *workspace, size_t workspace_bytes, pa_stream_t stream, bool clear_counters) {
   const pa_impl::LaunchEvents ev = g_next_events;    // the pair applies to this call only
   g_next_events = pa_impl::LaunchEvents{};
   if (int st = check_pool(pool)) return st;
@@ -317,6 +332,21 @@ int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
   }
   hipError_t e;
   const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (clear_counters && partition_size != 0) {
+    // the words that must start at zero: the control block and the unit
+    // counters of the balanced split, the arrival counters of fixed partitions
+    pa_impl::WorkspaceLayout w{};
+    workspace_layout(num_seqs, num_q_heads, pool->num_kv_heads, pool->head_dim, max_blocks_per_seq,
+                     pool->block_size, partition_size, &w);
+    char *base = static_cast<char *>(workspace);
+    if (partition_size == PA_PARTITION_AUTO) {
+      e = pa_impl::launch_zero(base, w.ctl_bytes, hs);
+      if (e == hipSuccess) e = pa_impl::launch_zero(base + w.ctl_bytes + w.partial_floats * 4, w.counter_bytes, hs);
+    } else {
+      e = pa_impl::launch_zero(base, w.counter_bytes, hs);
+    }
+    if (e != hipSuccess) return hip_fail(e);
+  }
   if (fast) {
     e = pa_impl::launch_decode_fast(q_dtype, pool->dtype, a, hs, ev);
   } else {
@@ -329,6 +359,10 @@ int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
   if (e != hipSuccess) return hip_fail(e);
   return ok();
 }
+
+}  // namespace pa_impl
+
+extern "C" {
 
 int pa_decode_status(const void *workspace, size_t workspace_bytes, int32_t partition_size,
                      int32_t *status, pa_stream_t stream) {

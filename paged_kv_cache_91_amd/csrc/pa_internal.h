@@ -5,6 +5,8 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include "pa.h"
+
 namespace pa_impl {
 
 // Element storage codes; equal to the public pa_dtype values.
@@ -83,6 +85,8 @@ hipError_t launch_write(int src_dtype, int dst_dtype, const WriteArgs &a, hipStr
 hipError_t launch_copy(const CopyArgs &a, hipStream_t s);
 // *out = word ? *word : 0, one thread, on stream s
 hipError_t launch_status(const int32_t *word, int32_t *out, hipStream_t s);
+// zero `bytes` bytes at p (a multiple of 16, 16-byte aligned) with a fill kernel
+hipError_t launch_zero(void *p, int64_t bytes, hipStream_t s);
 
 // Events the launch records as its first kernel begins and its last kernel
 // ends (none when null).
@@ -136,6 +140,17 @@ constexpr int kStreamWavesPerCu = 4;
 // that loads one slot never caches a line of another slot that is not yet
 // published.
 constexpr int kSlotMlFloats = 32;
+
+// Record `msg` for pa_last_error() on this thread; returns status.
+int set_error(int status, const char *msg);
+
+// The body of pa_decode (pa_api.cpp).  With clear_counters, the words of
+// the workspace that must start at zero are zero-filled on the stream first
+// (after validation, so a failing call still enqueues nothing).
+int decode_entry(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                 const pa_kv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                 const int32_t *context_lens, float scale, void *out, int32_t partition_size,
+                 void *workspace, size_t workspace_bytes, pa_stream_t stream, bool clear_counters);
 
 // Workspace layout shared by the API layer and the kernels.
 struct WorkspaceLayout {

@@ -461,6 +461,14 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
       *reinterpret_cast<const uint4 *>(pool + src * a.block_bytes + off);
 }
 
+// zero fill, 16 bytes a thread (a kernel rather than a memset node, so the
+// fill is safe to capture in a graph)
+__global__ __launch_bounds__(256) void zero_kernel(uint4 *p, int64_t n16) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 // the balanced split's workspace status word, copied where the caller asks
 __global__ __launch_bounds__(64) void status_kernel(const int32_t *word, int32_t *out) {
   if (threadIdx.x == 0) *out = word ? __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
@@ -528,6 +536,15 @@ hipError_t launch_write(int src_dtype, int dst_dtype, const WriteArgs &a, hipStr
 hipError_t launch_copy(const CopyArgs &a, hipStream_t s) {
   const dim3 grid(a.num_pairs, 2, static_cast<unsigned>((a.block_bytes + 4095) / 4096));
   hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(void *p, int64_t bytes, hipStream_t s) {
+  const int64_t n16 = bytes / 16;
+  if (n16 <= 0) return hipSuccess;
+  const int64_t blocks = (n16 + 255) / 256;
+  hipLaunchKernelGGL(zero_kernel, dim3(static_cast<unsigned>(blocks < 1024 ? blocks : 1024)), dim3(256), 0, s,
+                     static_cast<uint4 *>(p), n16);
   return hipGetLastError();
 }
 

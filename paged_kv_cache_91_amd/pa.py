@@ -31,7 +31,8 @@ _ELEM = {PA_F32: 4, PA_F16: 2, PA_BF16: 2, PA_FP8_E4M3: 1}
 
 EXPORTED = ("pa_write_kv", "pa_decode", "pa_decode_workspace_bytes", "pa_copy_blocks",
             "pa_status_string", "pa_last_error", "pa_version", "pa_time_next_decode",
-            "pa_decode_status", "pa_set_wait_polls")
+            "pa_decode_status", "pa_set_wait_polls", "pa_decode_noalloc")
+PA_NOALLOC_SCRATCH_BYTES = 32 << 20
 PA_WS_CLEAN, PA_WS_MISPLACED, PA_WS_TIMED_OUT = 0, 1, 2
 
 
@@ -93,6 +94,8 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_status.restype = ctypes.c_int
         L.pa_set_wait_polls.argtypes = [i32]
         L.pa_set_wait_polls.restype = ctypes.c_int
+        L.pa_decode_noalloc.argtypes = [vp, i32, i32, i32, pool_p, vp, i32, vp, ctypes.c_float, vp, i32, vp]
+        L.pa_decode_noalloc.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -226,6 +229,26 @@ def pa_decode(q: torch.Tensor, pool: KvPool, block_tables: torch.Tensor,
            "pa_decode")
     if own_ws is not None:
         workspace.record_stream(own_ws)
+    return out
+
+
+def pa_decode_noalloc(q: torch.Tensor, pool: KvPool, block_tables: torch.Tensor,
+                      context_lens: torch.Tensor, scale: float, out: torch.Tensor,
+                      partition_size: int = 0, q_dtype: Optional[str] = None, stream=None) -> torch.Tensor:
+    """pa_decode with the library's static scratch instead of a workspace;
+    ``out`` is required (nothing is allocated)."""
+    if q.dim() != 3 or out is None or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q must be [num_seqs, num_q_heads, head_dim] and out match it")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    s, hq, _ = q.shape
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or context_lens.shape != (s,):
+        raise ValueError("block_tables must be [S, max_blocks], context_lens [S]")
+    _check(lib().pa_decode_noalloc(_ptr(q, "q"), dtype_code(q, q_dtype), s, hq, ctypes.byref(pool),
+                                   _ptr(block_tables, "block_tables"), int(block_tables.shape[1]),
+                                   _ptr(context_lens, "context_lens"), float(scale), _ptr(out, "out"),
+                                   int(partition_size), _stream(stream)),
+           "pa_decode_noalloc")
     return out
 
 

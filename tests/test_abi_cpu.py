@@ -158,3 +158,19 @@ def test_status_query_and_wait_polls_validation():
     assert lib.pa_set_wait_polls(-1) == -1
     assert lib.pa_set_wait_polls(5) == 0
     assert lib.pa_set_wait_polls(0) == 0                                    # back to the default
+
+
+def test_noalloc_validation_without_gpu():
+    """Calls of pa_decode_noalloc that fail before touching the GPU."""
+    lib = pa.lib()
+    p = _pool()
+    args = lambda **kw: dict(dict(q=FAKE, qd=pa.PA_BF16, s=4, hq=8, pool=ctypes.byref(p), bt=FAKE, maxb=8,
+                                  ctx=FAKE, scale=0.1, out=FAKE * 2, part=0, stream=None), **kw)
+    call = lambda a: lib.pa_decode_noalloc(a["q"], a["qd"], a["s"], a["hq"], a["pool"], a["bt"], a["maxb"],
+                                           a["ctx"], a["scale"], a["out"], a["part"], a["stream"])
+    assert call(args(pool=None)) == -1
+    assert call(args(q=None)) == -1
+    assert call(args(s=0)) == 0
+    # a fixed-partition split far beyond the static scratch
+    assert call(args(s=60000, maxb=4096, part=16)) == -3
+    assert b"static scratch" in lib.pa_last_error()
