@@ -35,7 +35,11 @@ from .pa_oracle import (  # noqa: F401
     e4m3_encode,
     to_float64,
     gather_kv,
+    gather_kv_range,
+    window_start,
     oracle_decode,
+    oracle_prefill,
+    oracle_swap,
     oracle_partials,
     oracle_lse_merge,
     oracle_write,

@@ -183,6 +183,35 @@ def gather_kv(pool: np.ndarray, table_row: np.ndarray, num_tokens: int) -> np.nd
     return per_head[:, :num_tokens, :]
 
 
+def gather_kv_range(pool: np.ndarray, table_row: np.ndarray, start: int, stop: int) -> np.ndarray:
+    """Contiguous ``[num_kv_heads, stop - start, head_dim]`` of positions
+    start .. stop-1 of one sequence, read through its block table.
+
+    Only the blocks holding those positions are looked up: entries
+    ``start // bs .. ceil(stop / bs) - 1``.  Entries before ``start // bs``
+    are never read, so a table whose early entries name released blocks
+    (the sliding window of zerocoder.ru "Что такое PagedAttention", section
+    "Где подход не решает задачу", and vasteelab.pages.dev, section "hybrid
+    modelではblock設計が複雑になる": blocks that have left the attention
+    window are freed) gathers the same values.  With start = 0 this is
+    :func:`gather_kv`.
+    """
+    num_blocks, num_kv_heads, block_size, head_dim = pool.shape
+    if not 0 <= start <= stop:
+        raise ValueError("need 0 <= start <= stop")
+    first = start // block_size
+    last = blocks_needed(stop, block_size)                # one past the last block
+    ids = np.asarray(table_row[first:last], dtype=np.int64)
+    if ids.shape[0] != last - first:
+        raise ValueError("block table shorter than ceil(stop / block_size)")
+    if ids.size and (ids.min() < 0 or ids.max() >= num_blocks):
+        raise ValueError("block table names a block outside the pool")
+    blocks = pool[ids]                                    # [nb, Hkv, bs, D]
+    per_head = blocks.transpose(1, 0, 2, 3).reshape(num_kv_heads, ids.shape[0] * block_size, head_dim)
+    off = start - first * block_size
+    return per_head[:, off:off + (stop - start), :]
+
+
 # ---------------------------------------------------------------------------
 # decode attention
 # ---------------------------------------------------------------------------
@@ -201,10 +230,14 @@ def _check_decode_shapes(q, k_pool, v_pool, block_tables, context_lens):
     return num_seqs, num_q_heads, head_dim, num_kv_heads
 
 
-def _sequence_kv(k_pool, v_pool, kv_dtype, table_row, n, k_scale, v_scale):
-    """Float64 K and V of one sequence, ``[Hkv, n, D]`` each."""
-    k = to_float64(gather_kv(k_pool, table_row, n), kv_dtype)
-    v = to_float64(gather_kv(v_pool, table_row, n), kv_dtype)
+def _sequence_kv(k_pool, v_pool, kv_dtype, table_row, n, k_scale, v_scale, start=0):
+    """Float64 K and V of positions start .. n-1 of one sequence, ``[Hkv, n - start, D]`` each."""
+    if start == 0:
+        k = to_float64(gather_kv(k_pool, table_row, n), kv_dtype)
+        v = to_float64(gather_kv(v_pool, table_row, n), kv_dtype)
+    else:
+        k = to_float64(gather_kv_range(k_pool, table_row, start, n), kv_dtype)
+        v = to_float64(gather_kv_range(v_pool, table_row, start, n), kv_dtype)
     if kv_dtype == "fp8_e4m3":
         # per-tensor scale: stored code value times the tensor's fp32 scale
         k = k * float(np.float32(k_scale))
@@ -212,8 +245,24 @@ def _sequence_kv(k_pool, v_pool, kv_dtype, table_row, n, k_scale, v_scale):
     return k, v
 
 
+def window_start(n: int, window: int) -> int:
+    """First position a query at position n-1 sees under a sliding window of
+    ``window`` positions (0: no window): max(0, n - window).
+
+    zerocoder.ru, section "Где подход не решает задачу" (a limited attention
+    window, whose blocks are released once they leave it) and
+    vasteelab.pages.dev, section "hybrid modelではblock設計が複雑になる"
+    (sliding-window layers keep only the most recent tokens).  The pages do
+    not fix whether the window counts the query's own position; here it does:
+    the query and the window - 1 positions before it.
+    """
+    if window < 0:
+        raise ValueError("window must be >= 0")
+    return max(0, n - window) if window else 0
+
+
 def oracle_decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, context_lens,
-                  scale, k_scale=1.0, v_scale=1.0) -> np.ndarray:
+                  scale, k_scale=1.0, v_scale=1.0, window=0) -> np.ndarray:
     """Single-token decode attention over a paged cache, in float64.
 
     For each sequence s and query head h (KV head ``h // (Hq/Hkv)``; query
@@ -230,7 +279,9 @@ def oracle_decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, context_le
     the attention result unchanged ([PD] "PagedAttention"); the softmax
     subtracts its maximum first, which changes nothing mathematically.
     ``scale`` is taken as the float32 value the GPU receives.  A sequence with
-    n = 0 yields a zero row.  Returns float64 ``[S, Hq, D]``.
+    n = 0 yields a zero row.  With ``window`` > 0 only positions
+    :func:`window_start` .. n-1 take part (and only their blocks are read).
+    Returns float64 ``[S, Hq, D]``.
     """
     num_seqs, num_q_heads, head_dim, num_kv_heads = _check_decode_shapes(
         q, k_pool, v_pool, block_tables, context_lens)
@@ -242,12 +293,65 @@ def oracle_decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, context_le
         n = int(context_lens[s])
         if n == 0:
             continue
-        k, v = _sequence_kv(k_pool, v_pool, kv_dtype, block_tables[s], n, k_scale, v_scale)
+        k, v = _sequence_kv(k_pool, v_pool, kv_dtype, block_tables[s], n, k_scale, v_scale,
+                            start=window_start(n, window))
         for h in range(num_q_heads):
             kvh = h // group
             z = scale64 * (k[kvh] @ qf[s, h])
             p = np.exp(z - z.max())
             out[s, h] = (p @ v[kvh]) / p.sum()
+    return out
+
+
+def oracle_prefill(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, context_lens, query_start,
+                   scale, k_scale=1.0, v_scale=1.0, window=0) -> np.ndarray:
+    """Causal multi-query attention over a paged cache (a prompt, or a chunk
+    of one after a cached prefix), in float64.
+
+    Sequence s holds n = context_lens[s] positions in its blocks, the new
+    ones already written.  Its L = query_start[s+1] - query_start[s] queries
+    are rows query_start[s] .. query_start[s+1]-1 of ``q`` ([T, Hq, D]) and
+    stand for its last L positions: query i sits at position p = n - L + i.
+    Each attends positions lo .. p (lo = 0, or p + 1 - window with a sliding
+    window), with the scale, grouping and float64 softmax of
+    :func:`oracle_decode`:
+
+        out[row, h] = sum_{lo <= j <= p} softmax_j(scale * <q[row, h], K_j>) V_j
+
+    zerocoder.ru, section "Зачем KV cache вообще нужен": in full causal
+    attention each position uses the keys and values of the positions before
+    it; ultralytics.com "PagedAttention", section "관련 기법": engines run
+    FlashAttention-style kernels that read these from the paged blocks.  The
+    last query of a sequence is exactly the decode step of
+    :func:`oracle_decode`.  Returns float64 ``[T, Hq, D]``.
+    """
+    num_tokens, num_q_heads, head_dim = q.shape
+    num_kv_heads = k_pool.shape[1]
+    if num_q_heads % num_kv_heads:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    group = num_q_heads // num_kv_heads
+    qs = np.asarray(query_start, dtype=np.int64)
+    if qs.shape != (len(context_lens) + 1,) or qs[0] != 0 or qs[-1] != num_tokens or np.any(np.diff(qs) < 0):
+        raise ValueError("query_start must be a nondecreasing [S + 1] prefix sum from 0 to T")
+    scale64 = float(np.float32(scale))
+    qf = to_float64(q, q_dtype)
+    out = np.zeros((num_tokens, num_q_heads, head_dim), dtype=np.float64)
+    for s in range(len(context_lens)):
+        n, L = int(context_lens[s]), int(qs[s + 1] - qs[s])
+        if L > n:
+            raise ValueError("a sequence has more queries than positions")
+        if L == 0:
+            continue
+        first = window_start(n - L + 1, window)        # first position the first query sees
+        k, v = _sequence_kv(k_pool, v_pool, kv_dtype, block_tables[s], n, k_scale, v_scale, start=first)
+        for i in range(L):
+            p = n - L + i
+            lo = window_start(p + 1, window)
+            for h in range(num_q_heads):
+                kvh = h // group
+                z = scale64 * (k[kvh, lo - first:p + 1 - first] @ qf[qs[s] + i, h])
+                e = np.exp(z - z.max())
+                out[qs[s] + i, h] = (e @ v[kvh, lo - first:p + 1 - first]) / e.sum()
     return out
 
 
@@ -381,3 +485,36 @@ def oracle_copy(k_pool, v_pool, src_dst_pairs):
         k_pool[dst] = k_pool[src]
         v_pool[dst] = v_pool[src]
     return k_pool, v_pool
+
+
+# ---------------------------------------------------------------------------
+# swap between the GPU pool and host memory
+# ---------------------------------------------------------------------------
+
+def oracle_swap(src_k, src_v, dst_k, dst_v, src_dst_pairs):
+    """Copy whole blocks from one pool pair to another (the GPU pool and a
+    host swap area of the same block shape); returns new ``(dst_k, dst_v)``.
+
+    gufacode.com "PagedAttention:KV cache 的页表革命", section "Swap 到
+    CPU:兜底溢出": when the pool runs out, every block of a low-priority
+    sequence is copied to the CPU swap area and its GPU blocks are freed;
+    later the sequence is copied back and continues decoding.
+    vasteelab.pages.dev, section "blockが足りなくなったとき": swapping to the
+    CPU costs transfer time and CPU memory.  Sources may repeat (a block
+    copied to several places); destinations must be distinct.
+    """
+    if src_k.shape[1:] != dst_k.shape[1:] or src_k.dtype != dst_k.dtype:
+        raise ValueError("pools differ in block shape or dtype")
+    dst_k = dst_k.copy()
+    dst_v = dst_v.copy()
+    pairs = np.asarray(src_dst_pairs, dtype=np.int64).reshape(-1, 2)
+    if pairs.size:
+        if pairs[:, 0].min() < 0 or pairs[:, 0].max() >= src_k.shape[0] or \
+                pairs[:, 1].min() < 0 or pairs[:, 1].max() >= dst_k.shape[0]:
+            raise ValueError("block id outside its pool")
+        if len(np.unique(pairs[:, 1])) != len(pairs):
+            raise ValueError("destinations must be distinct")
+    for src, dst in pairs:
+        dst_k[dst] = src_k[src]
+        dst_v[dst] = src_v[src]
+    return dst_k, dst_v

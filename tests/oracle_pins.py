@@ -448,9 +448,164 @@ def pin_write_copy(ora):
         assert np.array_equal(a, b)
 
 
+# ---------------------------------------------------------------------------
+# sliding-window decode and paged prefill
+# ---------------------------------------------------------------------------
+
+def _bruteforce_rows(q_rows, kp, vp, table, hq, hkv, bs, scale, spans):
+    """fsum attention of query rows q_rows[i] ([Hq, D]) over positions
+    spans[i] = (lo, hi) of one paged sequence (the pages' gather, scalar loops)."""
+    d = q_rows.shape[-1]
+    out = np.zeros((len(spans), hq, d))
+    sc = float(np.float32(scale))
+    for i, (lo, hi) in enumerate(spans):
+        for h in range(hq):
+            kvh = h // (hq // hkv)
+            pos = list(range(lo, hi))
+            logits = [sc * math.fsum(float(q_rows[i, h, j]) * float(kp[int(table[t // bs]), kvh, t % bs, j])
+                                     for j in range(d)) for t in pos]
+            mx = max(logits)
+            e = [math.exp(z - mx) for z in logits]
+            den = math.fsum(e)
+            for j in range(d):
+                out[i, h, j] = math.fsum(e[k] * float(vp[int(table[t // bs]), kvh, t % bs, j])
+                                         for k, t in enumerate(pos)) / den
+    return out
+
+
+def pin_window_decode(ora):
+    """Sliding window: positions max(0, n - W) .. n-1 only (the query and the
+    W - 1 before it), and the blocks wholly before them are never read."""
+    lens = [1, 5, 16, 23, 40]
+    hq, hkv, d, bs = 4, 2, 6, 4
+    q, k_seq, v_seq, tables, nblocks = _random_paged(21, lens, hq, hkv, d, bs)
+    kp, vp = _place_contiguous(k_seq, v_seq, tables, nblocks, bs)
+    L = np.array(lens)
+    full = ora.oracle_decode(q, "f32", kp, vp, "f32", tables, L, 0.4)
+    for W in (1, 3, 8, 17):
+        out = ora.oracle_decode(q, "f32", kp, vp, "f32", tables, L, 0.4, window=W)
+        for s, n in enumerate(lens):
+            ref = _bruteforce_rows(q[s:s + 1], kp, vp, tables[s], hq, hkv, bs, 0.4, [(max(0, n - W), n)])
+            assert np.max(np.abs(out[s] - ref[0])) <= 1e-12
+            if W >= n:
+                assert np.array_equal(out[s], full[s])
+        # entries of blocks wholly before the window: released, may name anything
+        t2 = tables.copy()
+        for s, n in enumerate(lens):
+            t2[s, :max(0, n - W) // bs] = -1
+        assert np.array_equal(ora.oracle_decode(q, "f32", kp, vp, "f32", t2, L, 0.4, window=W), out)
+    # W = 1: exactly the V row of the last position
+    out = ora.oracle_decode(q, "f32", kp, vp, "f32", tables, L, 0.4, window=1)
+    for s, n in enumerate(lens):
+        for h in range(hq):
+            assert np.array_equal(out[s, h], v_seq[s][h // 2, n - 1].astype(np.float64))
+    # torch SDPA in float64 with the window as a boolean mask
+    for s, n in enumerate(lens):
+        W = 7
+        mask = torch.zeros((1, n), dtype=torch.bool)
+        mask[0, max(0, n - W):] = True
+        qt = torch.from_numpy(q[s].astype(np.float64))[None, :, None, :]
+        kt = torch.from_numpy(k_seq[s].astype(np.float64)).repeat_interleave(2, dim=0)[None]
+        vt = torch.from_numpy(v_seq[s].astype(np.float64)).repeat_interleave(2, dim=0)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=float(np.float32(0.4)))
+        out = ora.oracle_decode(q[s:s + 1], "f32", kp, vp, "f32", tables[s:s + 1], L[s:s + 1], 0.4, window=W)
+        assert np.max(np.abs(out[0] - ref[0, :, 0, :].numpy())) <= 1e-12
+
+
+def _prefill_case(seed, lens, qlens, hq, hkv, d, bs):
+    q_dec, k_seq, v_seq, tables, nblocks = _random_paged(seed, lens, hq, hkv, d, bs)
+    kp, vp = _place_contiguous(k_seq, v_seq, tables, nblocks, bs)
+    rng = np.random.default_rng(seed + 1)
+    q = rng.standard_normal((int(sum(qlens)), hq, d)).astype(np.float32)
+    qs = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    return q, k_seq, v_seq, tables, kp, vp, qs
+
+
+def pin_prefill(ora):
+    """Causal prefill: torch SDPA (is_causal) on whole prompts, brute force on
+    chunks and windows, the [PD] scalar head, and the decode step as its last
+    query."""
+    lens = [1, 9, 16, 33]
+    hq, hkv, d, bs = 6, 2, 8, 8
+    q, k_seq, v_seq, tables, kp, vp, qs = _prefill_case(31, lens, lens, hq, hkv, d, bs)
+    out = ora.oracle_prefill(q, "f32", kp, vp, "f32", tables, np.array(lens), qs, 0.35)
+    for s, n in enumerate(lens):
+        qt = torch.from_numpy(q[qs[s]:qs[s + 1]].astype(np.float64)).permute(1, 0, 2)[None]
+        kt = torch.from_numpy(k_seq[s].astype(np.float64)).repeat_interleave(3, dim=0)[None]
+        vt = torch.from_numpy(v_seq[s].astype(np.float64)).repeat_interleave(3, dim=0)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=float(np.float32(0.35)))
+        assert np.max(np.abs(out[qs[s]:qs[s + 1]] - ref[0].permute(1, 0, 2).numpy())) <= 1e-12
+    # chunks after a cached prefix: brute force over positions 0 .. p
+    qlens = [1, 4, 16, 7]
+    q, k_seq, v_seq, tables, kp, vp, qs = _prefill_case(32, lens, qlens, hq, hkv, d, bs)
+    for W in (0, 5):
+        out = ora.oracle_prefill(q, "f32", kp, vp, "f32", tables, np.array(lens), qs, 0.35, window=W)
+        for s, (n, L) in enumerate(zip(lens, qlens)):
+            spans = [(max(0, p + 1 - W) if W else 0, p + 1) for p in range(n - L, n)]
+            ref = _bruteforce_rows(q[qs[s]:qs[s + 1]], kp, vp, tables[s], hq, hkv, bs, 0.35, spans)
+            assert np.max(np.abs(out[qs[s]:qs[s + 1]] - ref)) <= 1e-12
+    # one query per sequence: the decode step
+    q1 = q[qs[1:] - 1]
+    one = ora.oracle_prefill(q1, "f32", kp, vp, "f32", tables, np.array(lens), np.arange(5, dtype=np.int32), 0.35)
+    dec = ora.oracle_decode(q1, "f32", kp, vp, "f32", tables, np.array(lens), 0.35)
+    assert np.max(np.abs(one - dec)) <= 1e-14
+    # [PD]'s scalar head as a prompt: query p sees V = 1 .. p+1 with equal weights
+    ex = golden()["pd_scalar"]
+    bs1, n = ex["block_size"], ex["num_tokens"]
+    placement = ex["placements"][0]
+    kp1 = np.full((8, 1, bs1, 1), np.nan, np.float32)
+    vp1 = np.full((8, 1, bs1, 1), np.nan, np.float32)
+    for pos in range(n):
+        kp1[placement[pos // bs1], 0, pos % bs1, 0] = ex["keys"]
+        vp1[placement[pos // bs1], 0, pos % bs1, 0] = ex["values"][pos]
+    qq = np.full((n, 1, 1), ex["query"], np.float32)
+    out = ora.oracle_prefill(qq, "f32", kp1, vp1, "f32", np.array([placement], np.int32), np.array([n]),
+                             np.array([0, n], np.int32), 1.0)
+    assert out[:, 0, 0].tolist() == [(p + 2) / 2 for p in range(n)]
+    assert out[-1, 0, 0] == ex["expected_output"]
+
+
+def pin_prefill_relabel(ora):
+    lens, qlens = [13, 30], [13, 9]
+    q, k_seq, v_seq, tables, kp, vp, qs = _prefill_case(33, lens, qlens, 4, 4, 8, 4)
+    a = ora.oracle_prefill(q, "f32", kp, vp, "f32", tables, np.array(lens), qs, 0.5)
+    perm = np.random.default_rng(34).permutation(kp.shape[0])
+    kp2, vp2 = np.empty_like(kp), np.empty_like(vp)
+    kp2[perm], vp2[perm] = kp, vp
+    b = ora.oracle_prefill(q, "f32", kp2, vp2, "f32", perm[tables].astype(np.int32), np.array(lens), qs, 0.5)
+    assert np.array_equal(a, b)
+
+
+def pin_swap(ora):
+    """[GC] swap: all blocks of a sequence go to the host area and come back
+    (to other GPU blocks): the bytes survive, decode through the new table is
+    unchanged, and nothing else moves."""
+    lens = [20, 9]
+    q, k_seq, v_seq, tables, nblocks = _random_paged(41, lens, 4, 2, 8, 4, extra_blocks=8)
+    kp, vp = _place_contiguous(k_seq, v_seq, tables, nblocks, 4)
+    ids = tables[0, :5]
+    hk = np.zeros((6, 2, 4, 8), np.float32)
+    hv = np.zeros_like(hk)
+    hk2, hv2 = ora.oracle_swap(kp, vp, hk, hv, np.stack([ids, np.arange(5)], 1))
+    assert np.array_equal(hk2[:5], kp[ids]) and np.array_equal(hv2[:5], vp[ids])
+    assert not hk2[5].any() and not hk[:5].any()
+    used = set(tables[0, :5]) | set(tables[1, :3])
+    fresh = np.array([b for b in range(nblocks) if b not in used][:5])
+    kp3, vp3 = ora.oracle_swap(hk2, hv2, kp, vp, np.stack([np.arange(5), fresh], 1))
+    assert np.array_equal(kp3[fresh], kp[ids]) and np.array_equal(vp3[fresh], vp[ids])
+    rest = [b for b in range(nblocks) if b not in fresh]
+    assert np.array_equal(kp3[rest], kp[rest])
+    t2 = tables.copy()
+    t2[0, :5] = fresh
+    a = ora.oracle_decode(q, "f32", kp, vp, "f32", tables, np.array(lens), 0.5)
+    b = ora.oracle_decode(q, "f32", kp3, vp3, "f32", t2, np.array(lens), 0.5)
+    assert np.array_equal(a, b)
+
+
 ALL_PINS = [
     pin_ul_pool_example, pin_zc_trace, pin_block_counts, pin_pool_sizing, pin_pd_scalar,
     pin_closed_forms, pin_zero_length, pin_bruteforce, pin_sdpa, pin_bf16_f16_decoding,
     pin_relabel_invariance, pin_split_merge, pin_fp8_table, pin_fp8_encode,
-    pin_fp8_write_decode, pin_write_copy,
+    pin_fp8_write_decode, pin_write_copy, pin_window_decode, pin_prefill, pin_prefill_relabel,
+    pin_swap,
 ]

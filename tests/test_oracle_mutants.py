@@ -40,6 +40,15 @@ MUTANTS = [
      "<< np.uint32(15)\n        return bits.view(np.float32).astype(np.float64)"),
     ("copy-direction", "k_pool[dst] = k_pool[src]", "k_pool[src] = k_pool[dst]"),
     ("blocks-floor", "return -(-num_tokens // block_size)", "return num_tokens // block_size"),
+    ("window-bound", "return max(0, n - window) if window else 0",
+     "return max(0, n - window - 1) if window else 0"),
+    ("range-offset", "off = start - first * block_size", "off = start - first"),
+    ("causal-limit", "z = scale64 * (k[kvh, lo - first:p + 1 - first]",
+     "z = scale64 * (k[kvh, lo - first:p + 2 - first]"),
+    ("query-position", "p = n - L + i", "p = i"),
+    ("prefill-group", "kvh = h // group\n                z = scale64 * (k[kvh, lo",
+     "kvh = h % num_kv_heads\n                z = scale64 * (k[kvh, lo"),
+    ("swap-direction", "dst_k[dst] = src_k[src]", "dst_k[dst] = dst_k[src]"),
 ]
 
 
