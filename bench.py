@@ -67,7 +67,7 @@ def parse():
                     help="with --workload other than llama3-8b: comma-separated partition sizes to time "
                          "(default: -1, 0 and the batch's own or 256)")
     ap.add_argument("--workload", default="llama3-8b",
-                    choices=["llama3-8b", "mha-13b", "prefix-cow", "fp8-long"],
+                    choices=["llama3-8b", "mha-13b", "prefix-cow", "fp8-long", "window", "swap"],
                     help="llama3-8b: the step above (default).  The others time pa_decode alone on the "
                          "13B-shaped fp16 batch, the prefix-sharing batch or the long-context fp8 batch "
                          "(one JSON line per partition setting)")
@@ -128,6 +128,8 @@ def main():
 
     if args.calibrate_copy:
         return calibrate_copy(args.calibrate_copy, pa, torch, dev)
+    if args.workload == "swap":
+        return swap_workload(args, pa, torch, dev)
     if args.workload != "llama3-8b":
         return other_workload(args, pa, W, torch, dev)
 
@@ -328,7 +330,11 @@ def other_workload(args, pa, W, torch, dev):
     batch's (about 40 MB of distinct blocks): its numbers are cache-warm."""
     import numpy as np
     t0 = time.time()
-    wl = {"mha-13b": W.config3, "prefix-cow": W.config4, "fp8-long": W.config5}[args.workload]()
+    window = 0
+    if args.workload == "window":
+        wl, window = window_batch(W), WINDOW
+    else:
+        wl = {"mha-13b": W.config3, "prefix-cow": W.config4, "fp8-long": W.config5}[args.workload]()
     log(f"[bench] {args.workload} generated in {time.time() - t0:.1f}s: S={wl.num_seqs} "
         f"kv_bytes={wl.kv_bytes() / 1e9:.3f} GB")
     storage = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "fp8_e4m3": torch.uint8}
@@ -365,23 +371,33 @@ def other_workload(args, pa, W, torch, dev):
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
     kv_bytes = wl.kv_bytes()
+    if window:
+        # bytes the windowed decode reads: min(n, window) positions per sequence
+        seen = np.minimum(wl.context_lens.astype(np.int64), window)
+        kv_bytes = int(seen.sum()) * 2 * wl.num_kv_heads * wl.head_dim * W.ELEMENT_SIZE[wl.kv_dtype]
     parts = [-1, 0] + ([wl.partition_size] if wl.partition_size > 0 else [256])
     if args.partitions:
         parts = [int(x) for x in args.partitions.split(",")]
     for part in parts:
         ws = pa.new_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                               wl.max_blocks_per_seq, wl.block_size, part, device=dev) if part else None
+        def call():
+            if window:
+                pa.pa_decode_window(q, pool, tb, ctx, window, wl.scale, out=out, partition_size=part,
+                                    workspace=ws, q_dtype=wl.q_dtype, stream=stream)
+            else:
+                pa.pa_decode(q, pool, tb, ctx, wl.scale, out=out, partition_size=part, workspace=ws,
+                             q_dtype=wl.q_dtype, stream=stream)
+
         for _ in range(max(args.warmup, 3)):
-            pa.pa_decode(q, pool, tb, ctx, wl.scale, out=out, partition_size=part, workspace=ws,
-                         q_dtype=wl.q_dtype, stream=stream)
+            call()
         steps = max(1, min(args.steps, 50))
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
         torch.cuda.synchronize()
         for a, b in ev:
             a.record(stream)
-            pa.pa_decode(q, pool, tb, ctx, wl.scale, out=out, partition_size=part, workspace=ws,
-                         q_dtype=wl.q_dtype, stream=stream)
+            call()
             b.record(stream)
         torch.cuda.synchronize()
         us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
@@ -389,7 +405,7 @@ def other_workload(args, pa, W, torch, dev):
         gbs = kv_bytes / (med * 1e-6) / 1e9
         assert bool(torch.isfinite(out.float()).all()), "non-finite output"
         print(json.dumps({
-            "workload": args.workload, "partition_size": part, "kv_bytes": kv_bytes,
+            "workload": args.workload, "partition_size": part, "kv_bytes": kv_bytes, "window": window,
             "kv_dtype": wl.kv_dtype, "num_seqs": wl.num_seqs, "num_q_heads": wl.num_q_heads,
             "num_kv_heads": wl.num_kv_heads, "block_size": wl.block_size,
             "decode_us": {"median": round(med, 2), "p10": round(us[len(us) // 10], 2),
@@ -398,6 +414,70 @@ def other_workload(args, pa, W, torch, dev):
             "decode_tokens_per_s_per_layer": round(wl.num_seqs / (med * 1e-6), 1),
             "cache": "warm (fits the last-level cache)" if kv_bytes < (256 << 20) else "pools exceed the last-level cache",
         }), flush=True)
+
+
+# sliding-window batch: the 8B layer shape with long contexts and a window
+# of 4096 positions (the decode reads min(n, 4096) positions per sequence)
+WINDOW = 4096
+
+
+def window_batch(W):
+    import numpy as np
+    rng = np.random.default_rng(9)
+    lens = rng.integers(4096, 16385, size=32)
+    need = int(sum(-(-int(n) // 16) for n in lens))
+    return W.build_decode(9, name="window-4096-bf16", q_dtype="bf16", kv_dtype="bf16", num_q_heads=32,
+                          num_kv_heads=8, head_dim=128, block_size=16, num_blocks=need + 64,
+                          context_lens=lens, rng=rng)
+
+
+def swap_workload(args, pa, torch, dev):
+    """pa_swap_blocks between the GPU pool and a pinned host swap area, both
+    directions, on blocks of the 8B layer shape (8 KV heads x 16 x 128, bf16:
+    32 KiB each of K and V), 4096 scattered blocks (256 MiB) per call; a plain
+    contiguous copy of the same bytes between device and pinned host memory
+    (the DMA engines) is timed beside it as the link's practical ceiling."""
+    import numpy as np
+    nb_dev, nb_host, moved = 16384, 4096, 4096
+    kd = torch.zeros((nb_dev, 8, 16, 128), dtype=torch.bfloat16, device=dev)
+    vd = torch.zeros_like(kd)
+    kh = torch.zeros((nb_host, 8, 16, 128), dtype=torch.bfloat16, pin_memory=True)
+    vh = torch.zeros_like(kh).pin_memory()
+    gpu, host = pa.make_pool(kd, vd), pa.make_pool(kh, vh, host=True)
+    rng = np.random.default_rng(11)
+    out_pairs = np.stack([rng.permutation(nb_dev)[:moved], rng.permutation(nb_host)[:moved]], 1).astype(np.int64)
+    in_pairs = out_pairs[:, ::-1].copy()
+    po, pi = torch.from_numpy(out_pairs).to(dev), torch.from_numpy(in_pairs).to(dev)
+    block_bytes = 2 * 8 * 16 * 128 * 2
+    total = moved * block_bytes
+    stream = torch.cuda.current_stream()
+    flat_d = torch.empty(total, dtype=torch.uint8, device=dev)
+    flat_h = torch.empty(total, dtype=torch.uint8, pin_memory=True)
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+        return us[len(us) // 2]
+
+    reps = max(3, min(args.steps, 20))
+    res = {}
+    for name, fn in (("gpu_to_host", lambda: pa.pa_swap_blocks(gpu, host, po, stream=stream)),
+                     ("host_to_gpu", lambda: pa.pa_swap_blocks(host, gpu, pi, stream=stream)),
+                     ("dma_copy_gpu_to_host", lambda: flat_h.copy_(flat_d, non_blocking=True)),
+                     ("dma_copy_host_to_gpu", lambda: flat_d.copy_(flat_h, non_blocking=True))):
+        med = timed(fn, reps)
+        res[name] = {"median_us": round(med, 1), "gbs": round(total / (med * 1e-6) / 1e9, 2)}
+        log(f"[bench] swap {name}: {med:.1f} us")
+    print(json.dumps({"workload": "swap", "blocks_per_call": moved, "bytes_per_call": total,
+                      "block_bytes": block_bytes, "calls": reps, "results": res}), flush=True)
 
 
 def calibrate_copy(mib, pa, torch, dev):

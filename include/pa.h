@@ -198,6 +198,29 @@ int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
               void *workspace, size_t workspace_bytes, pa_stream_t stream);
 
 /*
+ * pa_decode_window -- pa_decode under a sliding attention window (zerocoder.ru
+ * "Что такое PagedAttention", section "Где подход не решает задачу": with a
+ * limited attention window, blocks that leave it are released;
+ * vasteelab.pages.dev, section "hybrid modelではblock設計が複雑になる").
+ *
+ * As pa_decode, except that sequence s attends only positions
+ * lo .. n-1 with lo = max(0, n - window): the current position and the
+ * window - 1 before it.  Table entries of blocks wholly before lo
+ * (j < lo / block_size) are never read, so they may name released blocks or
+ * hold any value.  With partition_size > 0 the partitions are
+ * [p*P, (p+1)*P) intersected with [lo, n), merged in increasing p.
+ *
+ *   window    >= 0; 0 attends the whole context (pa_decode).
+ * Every other argument, the workspace contract and the error behaviour are
+ * pa_decode's (the workspace is sized with pa_decode_workspace_bytes for the
+ * same arguments).
+ */
+int pa_decode_window(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                     const pa_kv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                     const int32_t *context_lens, int32_t window, float scale, void *out,
+                     int32_t partition_size, void *workspace, size_t workspace_bytes, pa_stream_t stream);
+
+/*
  * pa_copy_blocks -- copy-on-write block copy.
  *
  * For each pair i < num_pairs, (src, dst) = (src_dst_pairs[2i], src_dst_pairs[2i+1]):
@@ -274,6 +297,37 @@ int pa_decode_noalloc(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t 
                       const pa_kv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
                       const int32_t *context_lens, float scale, void *out, int32_t partition_size,
                       pa_stream_t stream);
+
+/*
+ * pa_swap_blocks -- whole-block copies from one pool pair to another of the
+ * same block shape: the GPU pool and a swap area in pinned host memory, in
+ * either direction (gufacode.com "PagedAttention:KV cache 的页表革命", section
+ * "Swap 到 CPU:兜底溢出": when the pool runs out, all blocks of a
+ * low-priority sequence are copied to CPU memory and freed, and copied back
+ * later; vasteelab.pages.dev, section "blockが足りなくなったとき").
+ *
+ * For each pair i < num_pairs, (s, d) = (src_dst_pairs[2i], src_dst_pairs[2i+1]):
+ *     dst->k_pool[d] = src->k_pool[s];  dst->v_pool[d] = src->v_pool[s]
+ * over every head and slot of the block, bit for bit.  One kernel moves all
+ * pairs; the host side of the copy is read or written over the host link by
+ * the kernel itself.
+ *
+ *   src, dst       descriptors with equal num_kv_heads, block_size, head_dim
+ *                  and dtype (num_blocks may differ).  Each pool pointer is
+ *                  device memory of the current device or host memory from
+ *                  hipHostMalloc (torch: pin_memory=True); anything else
+ *                  (pageable host memory) is refused with PA_ERR_INVALID_ARG
+ *                  before any launch.
+ *   src_dst_pairs  int64 [num_pairs][2], device or pinned host memory.
+ *                  Destinations must be distinct (and, within one pool, not
+ *                  also sources).  A pair naming a block outside its pool is
+ *                  skipped; within one pool so is s == d.
+ *   num_pairs      >= 0; 0 enqueues nothing.
+ * Host memory written by the kernel is complete once `stream` has reached
+ * the end of the call (synchronise before reading it on the host).
+ */
+int pa_swap_blocks(const pa_kv_pool *src, const pa_kv_pool *dst, const int64_t *src_dst_pairs,
+                   int32_t num_pairs, pa_stream_t stream);
 
 /* Static text for a pa_status value. */
 const char *pa_status_string(int status);

@@ -20,7 +20,16 @@ and read the bytes.  Behaviour follows the pages:
   "시퀀스 간 블록 공유"; gufacode.com, section "前缀共享:Copy-on-Write");
 * the structural checks of zerocoder.ru's worked trace: tables name existing
   blocks, reference counts agree with the tables, and freeing leaves no
-  dangling entries.
+  dangling entries;
+* when the pool runs out, every block of a sequence can be moved to a swap
+  area in host memory and its GPU blocks freed, then brought back later into
+  whatever GPU blocks are free (gufacode.com, section "Swap 到 CPU:兜底溢出";
+  vasteelab.pages.dev, section "blockが足りなくなったとき");
+* under a sliding attention window, blocks that lie wholly before the window
+  are released (zerocoder.ru, section "Где подход не решает задачу";
+  vasteelab.pages.dev, section "hybrid modelではblock設計が複雑になる"); their
+  table entries stay as RELEASED placeholders so logical block j is still
+  entry j, and the windowed decode never reads them.
 """
 
 from __future__ import annotations
@@ -51,11 +60,15 @@ class AllocatorStats:
     tokens: int                 # sum of sequence lengths
 
 
+RELEASED = -1   # table entry of a block released under a sliding window
+
+
 class BlockAllocator:
-    """Free list + reference counts + per-sequence block tables."""
+    """Free list + reference counts + per-sequence block tables (+ an
+    optional host swap area of ``host_blocks`` blocks)."""
 
     def __init__(self, num_blocks: int, block_size: int,
-                 free_order: Optional[Iterable[int]] = None):
+                 free_order: Optional[Iterable[int]] = None, host_blocks: int = 0):
         if num_blocks <= 0:
             raise ValueError("num_blocks must be positive")
         if block_size <= 1 or block_size & (block_size - 1):
@@ -73,6 +86,18 @@ class BlockAllocator:
         self._tables: Dict[int, List[int]] = {}
         self._lengths: Dict[int, int] = {}
         self._cow_copies = 0
+        self.host_blocks = 0
+        self._host_free: deque = deque()
+        self._swapped: Dict[int, Tuple[List[int], int]] = {}   # seq -> (host table, length)
+        self.add_host_area(host_blocks)
+
+    def add_host_area(self, host_blocks: int) -> None:
+        """Grow the host swap area by ``host_blocks`` slots (ids continue
+        from the current size)."""
+        if host_blocks < 0:
+            raise ValueError("host_blocks must be >= 0")
+        self._host_free.extend(range(self.host_blocks, self.host_blocks + host_blocks))
+        self.host_blocks += host_blocks
 
     # -- queries ---------------------------------------------------------
 
@@ -100,6 +125,8 @@ class BlockAllocator:
         if not 0 <= pos < self._lengths[seq_id]:
             raise AllocatorError(f"position {pos} outside sequence {seq_id}")
         table = self._tables[seq_id]
+        if table[pos // self.block_size] == RELEASED:
+            raise AllocatorError(f"position {pos} lies in a released block")
         return table[pos // self.block_size] * self.block_size + pos % self.block_size
 
     def slots(self, seq_id: int, start: int, stop: int) -> np.ndarray:
@@ -108,6 +135,8 @@ class BlockAllocator:
             raise AllocatorError("slot range outside the sequence")
         table = np.asarray(self._tables[seq_id], dtype=np.int64)
         pos = np.arange(start, stop, dtype=np.int64)
+        if (table[pos // self.block_size] == RELEASED).any():
+            raise AllocatorError("slot range reaches a released block")
         return table[pos // self.block_size] * self.block_size + pos % self.block_size
 
     def tables_array(self, seq_ids: Sequence[int], max_blocks: Optional[int] = None,
@@ -122,6 +151,13 @@ class BlockAllocator:
             out[i, :len(r)] = r
         return out
 
+    def swapped(self) -> List[int]:
+        return list(self._swapped)
+
+    @property
+    def num_host_free(self) -> int:
+        return len(self._host_free)
+
     def stats(self) -> AllocatorStats:
         used = int((self._refcount > 0).sum())
         return AllocatorStats(
@@ -131,7 +167,7 @@ class BlockAllocator:
             shared_blocks=int((self._refcount > 1).sum()),
             cow_copies=self._cow_copies,
             waste_slots=sum(len(t) * self.block_size - self._lengths[s]
-                            for s, t in self._tables.items()),
+                            for s, t in self._tables.items() if t),
             tokens=sum(self._lengths.values()),
         )
 
@@ -153,7 +189,7 @@ class BlockAllocator:
 
     def add_sequence(self, seq_id: int, num_tokens: int = 0) -> List[int]:
         """Register a sequence holding ``num_tokens`` tokens (a prompt)."""
-        if seq_id in self._tables:
+        if seq_id in self._tables or seq_id in self._swapped:
             raise AllocatorError(f"sequence {seq_id} exists")
         need = -(-num_tokens // self.block_size)
         if need > len(self._free):
@@ -217,22 +253,86 @@ class BlockAllocator:
 
     def fork(self, parent_id: int, child_id: int) -> List[int]:
         """New sequence sharing every block of ``parent_id`` (refcounts + 1)."""
-        if child_id in self._tables:
+        if child_id in self._tables or child_id in self._swapped:
             raise AllocatorError(f"sequence {child_id} exists")
         table = list(self._tables[parent_id])
         for b in table:
-            self._refcount[b] += 1
+            if b != RELEASED:
+                self._refcount[b] += 1
         self._tables[child_id] = table
         self._lengths[child_id] = self._lengths[parent_id]
         return list(table)
 
     def free(self, seq_id: int) -> None:
         """Return a finished sequence's blocks (shared ones lose one reference)."""
+        if seq_id in self._swapped:
+            host, _ = self._swapped.pop(seq_id)
+            self._host_free.extend(h for h in host if h != RELEASED)
+            return
         if seq_id not in self._tables:
             raise AllocatorError(f"sequence {seq_id} unknown or already freed")
         for b in self._tables.pop(seq_id):
-            self._release(b)
+            if b != RELEASED:
+                self._release(b)
         del self._lengths[seq_id]
+
+    # -- sliding window --------------------------------------------------
+
+    def release_before_window(self, seq_id: int, window: int) -> List[int]:
+        """Release the blocks of ``seq_id`` that lie wholly before its sliding
+        window: with n tokens the window starts at lo = max(0, n - window), so
+        logical blocks j < lo // block_size hold no position the next decode
+        step reads.  Their entries become RELEASED; shared blocks lose one
+        reference.  Returns the block ids released by this call."""
+        if window <= 0:
+            return []
+        table = self._tables[seq_id]
+        lo = max(0, self._lengths[seq_id] - window)
+        out = []
+        for j in range(lo // self.block_size):
+            b = table[j]
+            if b != RELEASED:
+                self._release(b)
+                table[j] = RELEASED
+                out.append(b)
+        return out
+
+    # -- swap to the host area ---------------------------------------------
+
+    def swap_out(self, seq_id: int) -> List[Tuple[int, int]]:
+        """Move every block of ``seq_id`` to host slots and free its GPU
+        blocks (shared ones lose one reference).  Returns the (GPU block,
+        host slot) copies to apply, e.g. with pa_swap_blocks, on the stream
+        ahead of any later write into the freed blocks.  All or nothing:
+        OutOfBlocks if the host area lacks the slots."""
+        table = self._tables[seq_id]
+        live = [b for b in table if b != RELEASED]
+        if len(live) > len(self._host_free):
+            raise OutOfBlocks(f"swap-out needs {len(live)} host slots, {len(self._host_free)} free")
+        host = [RELEASED if b == RELEASED else self._host_free.popleft() for b in table]
+        for b in live:
+            self._release(b)
+        self._swapped[seq_id] = (host, self._lengths.pop(seq_id))
+        del self._tables[seq_id]
+        return [(b, h) for b, h in zip(table, host) if b != RELEASED]
+
+    def swap_in(self, seq_id: int) -> List[Tuple[int, int]]:
+        """Bring a swapped-out sequence back into free GPU blocks.  Returns
+        the (host slot, GPU block) copies to apply before the sequence is
+        read; its host slots are free again once those copies are ordered
+        ahead of any later swap-out on the same stream.  All or nothing."""
+        if seq_id not in self._swapped:
+            raise AllocatorError(f"sequence {seq_id} is not swapped out")
+        host, n = self._swapped[seq_id]
+        live = [h for h in host if h != RELEASED]
+        if len(live) > len(self._free):
+            raise OutOfBlocks(f"swap-in needs {len(live)} blocks, {len(self._free)} free")
+        table = [RELEASED if h == RELEASED else self._take() for h in host]
+        del self._swapped[seq_id]
+        self._tables[seq_id] = table
+        self._lengths[seq_id] = n
+        self._host_free.extend(live)
+        return [(h, b) for h, b in zip(host, table) if h != RELEASED]
 
     # -- structural checks -----------------------------------------------
 
@@ -242,10 +342,22 @@ class BlockAllocator:
         for s, table in self._tables.items():
             if len(table) != -(-self._lengths[s] // self.block_size):
                 raise AllocatorError(f"sequence {s}: table does not cover its tokens")
-            for b in table:
+            live = [b for b in table if b != RELEASED]
+            if table[:len(table) - len(live)] != [RELEASED] * (len(table) - len(live)):
+                raise AllocatorError(f"sequence {s}: released entries must be a prefix")
+            if table and table[-1] == RELEASED:
+                raise AllocatorError(f"sequence {s}: the last block was released")
+            for b in live:
                 if not 0 <= b < self.num_blocks:
                     raise AllocatorError(f"sequence {s}: block {b} outside the pool")
                 counts[b] += 1
+        host_used = [h for host, _ in self._swapped.values() for h in host if h != RELEASED]
+        if set(self._swapped) & set(self._tables):
+            raise AllocatorError("a sequence is both resident and swapped out")
+        if len(set(host_used)) != len(host_used) or set(host_used) & set(self._host_free) or \
+                len(host_used) + len(self._host_free) != self.host_blocks or \
+                any(not 0 <= h < self.host_blocks for h in host_used):
+            raise AllocatorError("host swap slots are inconsistent")
         if not np.array_equal(counts, self._refcount):
             raise AllocatorError("reference counts disagree with the tables")
         free = list(self._free)

@@ -205,7 +205,17 @@ int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
               const int32_t *context_lens, float scale, void *out, int32_t partition_size,
               void *workspace, size_t workspace_bytes, pa_stream_t stream) {
   return pa_impl::decode_entry(q, q_dtype, num_seqs, num_q_heads, pool, block_tables, max_blocks_per_seq,
-                               context_lens, scale, out, partition_size, workspace, workspace_bytes,
+                               context_lens, 0, scale, out, partition_size, workspace, workspace_bytes,
+                               stream, false);
+}
+
+int pa_decode_window(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                     const pa_kv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                     const int32_t *context_lens, int32_t window, float scale, void *out,
+                     int32_t partition_size, void *workspace, size_t workspace_bytes, pa_stream_t stream) {
+  if (window < 0) return fail(PA_ERR_INVALID_ARG, "window must be >= 0");
+  return pa_impl::decode_entry(q, q_dtype, num_seqs, num_q_heads, pool, block_tables, max_blocks_per_seq,
+                               context_lens, window, scale, out, partition_size, workspace, workspace_bytes,
                                stream, false);
 }
 
@@ -217,7 +227,7 @@ int set_error(int status, const char *msg) { return fail(status, "%s", msg); }
 
 int decode_entry(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
                  const pa_kv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
-                 const int32_t *context_lens, float scale, void *out, int32_t partition_size,
+                 const int32_t *context_lens, int32_t window, float scale, void *out, int32_t partition_size,
                  void *workspace, size_t workspace_bytes, pa_stream_t stream, bool clear_counters) {
   const pa_impl::LaunchEvents ev = g_next_events;    // the pair applies to this call only
   g_next_events = pa_impl::LaunchEvents{};
@@ -277,6 +287,7 @@ int decode_entry(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * ks * log2e);
   a.v_scale = pool->dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
   a.wait_polls = g_wait_polls;
+  a.window = window;
 
   const bool fast = pa_impl::fast_decode_applies(q_dtype, pool->dtype, a);
   if (partition_size == PA_PARTITION_AUTO && !fast) {
@@ -393,13 +404,76 @@ int pa_copy_blocks(const pa_kv_pool *pool, const int64_t *src_dst_pairs, int32_t
   if (num_pairs == 0) return ok();
   if (!src_dst_pairs) return fail(PA_ERR_INVALID_ARG, "src_dst_pairs is NULL");
   pa_impl::CopyArgs a{};
-  a.k_pool = pool->k_pool;
-  a.v_pool = pool->v_pool;
+  a.src_k = a.dst_k = pool->k_pool;
+  a.src_v = a.dst_v = pool->v_pool;
   a.pairs = src_dst_pairs;
-  a.num_blocks = pool->num_blocks;
+  a.src_blocks = a.dst_blocks = pool->num_blocks;
   a.block_bytes = static_cast<int64_t>(pool->num_kv_heads) * pool->block_size * pool->head_dim *
                   element_size(pool->dtype);
   a.num_pairs = num_pairs;
+  a.same_pool = 1;
+  if (ceil_div(a.block_bytes, 4096) > 65535) return fail(PA_ERR_INVALID_ARG, "block too large");
+  hipError_t e = pa_impl::launch_copy(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return ok();
+}
+
+// Device address a kernel of the current device can use for `p`: device
+// memory of the current device as is, pinned host memory through its mapped
+// device address; anything else (pageable host memory, another device's
+// memory, an unknown pointer) is refused before any launch.
+static int kernel_address(const void *p, const char *what, void **out) {
+  if (!p) return fail(PA_ERR_INVALID_ARG, "%s is NULL", what);
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();            // leave no error behind for the caller's next call
+    return fail(PA_ERR_INVALID_ARG, "%s is not device memory or pinned host memory", what);
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_HIP, "no current device");
+  if (at.type == hipMemoryTypeDevice) {
+    if (at.device != dev) return fail(PA_ERR_INVALID_ARG, "%s lives on device %d, not the current %d", what, at.device, dev);
+    *out = const_cast<void *>(p);
+    return PA_OK;
+  }
+  if (at.type == hipMemoryTypeHost && at.devicePointer) {
+    // the mapped address of this exact byte (p may point inside the allocation)
+    const char *host_base = static_cast<const char *>(at.hostPointer ? at.hostPointer : p);
+    *out = static_cast<char *>(at.devicePointer) + (static_cast<const char *>(p) - host_base);
+    return PA_OK;
+  }
+  return fail(PA_ERR_INVALID_ARG, "%s is not device memory or pinned host memory (hipHostMalloc)", what);
+}
+
+int pa_swap_blocks(const pa_kv_pool *src, const pa_kv_pool *dst, const int64_t *src_dst_pairs,
+                   int32_t num_pairs, pa_stream_t stream) {
+  if (!src || !dst) return fail(PA_ERR_INVALID_ARG, "pool descriptor is NULL");
+  // the descriptors' own checks, with the pointer check done below instead
+  if (int st = check_pool(src)) return st;
+  if (int st = check_pool(dst)) return st;
+  if (src->num_kv_heads != dst->num_kv_heads || src->block_size != dst->block_size ||
+      src->head_dim != dst->head_dim || src->dtype != dst->dtype)
+    return fail(PA_ERR_INVALID_ARG, "source and destination pools differ in block shape or dtype");
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "num_pairs must be >= 0");
+  if (num_pairs == 0) return ok();
+  pa_impl::CopyArgs a{};
+  void *sk, *sv, *dk, *dv, *pairs;
+  if (int st = kernel_address(src->k_pool, "source K pool", &sk)) return st;
+  if (int st = kernel_address(src->v_pool, "source V pool", &sv)) return st;
+  if (int st = kernel_address(dst->k_pool, "destination K pool", &dk)) return st;
+  if (int st = kernel_address(dst->v_pool, "destination V pool", &dv)) return st;
+  if (int st = kernel_address(src_dst_pairs, "src_dst_pairs", &pairs)) return st;
+  a.src_k = sk;
+  a.src_v = sv;
+  a.dst_k = dk;
+  a.dst_v = dv;
+  a.pairs = static_cast<const int64_t *>(pairs);
+  a.src_blocks = src->num_blocks;
+  a.dst_blocks = dst->num_blocks;
+  a.block_bytes = static_cast<int64_t>(src->num_kv_heads) * src->block_size * src->head_dim *
+                  element_size(src->dtype);
+  a.num_pairs = num_pairs;
+  a.same_pool = (src->k_pool == dst->k_pool) ? 1 : 0;
   if (ceil_div(a.block_bytes, 4096) > 65535) return fail(PA_ERR_INVALID_ARG, "block too large");
   hipError_t e = pa_impl::launch_copy(a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);

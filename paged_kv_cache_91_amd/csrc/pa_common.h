@@ -62,6 +62,14 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return sign | static_cast<uint32_t>(m);
 }
 
+// First position a sliding window of `window` positions (0: none) leaves
+// visible to the query at position n - 1: the query and the window - 1
+// positions before it.  Blocks wholly before it may have been released, so
+// their table entries are never read.
+__host__ __device__ __forceinline__ int window_lo(int n, int window) {
+  return (window > 0 && n > window) ? n - window : 0;
+}
+
 // ---------------------------------------------------------------------------
 // storage traits: how one lane loads and widens its run of a K/V row
 // ---------------------------------------------------------------------------

@@ -367,15 +367,16 @@ struct Fast {
   // of one dim into one dword) and then widened exactly to the MFMA type.
   template <bool MASKED>
   static __device__ __forceinline__ void pv(const Tile &t, const uint32_t pb_lo, const uint32_t pb_hi,
-                                            int p0, int pend, f32x4_t (&acc)[8]) {
+                                            int p0, int pbeg, int pend, f32x4_t (&acc)[8]) {
     using V4 = typename M::V4;
     const V4 pb = __builtin_bit_cast(V4, make_uint2(pb_lo, pb_hi));
     auto mma = [&](int e, uint32_t a01, uint32_t a23) {
       acc[e] = M::run16(__builtin_bit_cast(V4, make_uint2(a01, a23)), pb, acc[e]);
     };
-    // rows past the context end have p = 0, but their stale bytes may hold
-    // NaN or Inf, so they are zeroed before the product
-    auto keep = [&](int c) { return !MASKED || p0 + c < pend; };
+    // rows outside [pbeg, pend) (past the context end, or before a sliding
+    // window) have p = 0, but their bytes may hold NaN or Inf, so they are
+    // zeroed before the product
+    auto keep = [&](int c) { return !MASKED || (p0 + c < pend && p0 + c >= pbeg); };
     if constexpr (kFp8) {
       uint32_t x[4][2];
 #pragma unroll
@@ -417,7 +418,7 @@ struct Fast {
   }
 
   template <bool MASKED>
-  static __device__ __forceinline__ void compute(const Tile &t, const V8 (&qb)[4], int tpos,
+  static __device__ __forceinline__ void compute(const Tile &t, const V8 (&qb)[4], int tpos, int pbeg,
                                                  int pend, int g4, float scale_log2,
                                                  float &m_run, float &l_run, f32x4_t (&acc)[8]) {
     f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -428,7 +429,7 @@ struct Fast {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       sc[r] = s[r] * scale_log2;
-      if constexpr (MASKED) sc[r] = (p0 + r < pend) ? sc[r] : -INFINITY;
+      if constexpr (MASKED) sc[r] = (p0 + r < pend && p0 + r >= pbeg) ? sc[r] : -INFINITY;
     }
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mx = xor32_max(xor16_max(mx));
@@ -445,12 +446,13 @@ struct Fast {
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] *= alpha;
     }
-    pv<MASKED>(t, M::pack2(p[0], p[1]), M::pack2(p[2], p[3]), p0, pend, acc);
+    pv<MASKED>(t, M::pack2(p[0], p[1]), M::pack2(p[2], p[3]), p0, pbeg, pend, acc);
   }
 
   // Accumulate `count` tiles of one (sequence, head group) into this wave's
   // online-softmax state: tile t_first + stride * i for i < count, each 16
-  // positions starting at 16 * tile; positions >= pend are masked.
+  // positions starting at 16 * tile; positions outside [pbeg, pend) are
+  // masked.
   //
   // The tiles stream through a ring of kRing buffers: the loads of tile
   // i + kRing are issued as soon as tile i has been computed, so kRing
@@ -461,7 +463,7 @@ struct Fast {
   // ahead with scalar loads.
   static __device__ __forceinline__ void accumulate(
       const DecodeArgs &a, const V8 (&qb)[4], const uint8_t *__restrict__ kb,
-      const uint8_t *__restrict__ vb, const int32_t *__restrict__ trow, int pend, int t_first,
+      const uint8_t *__restrict__ vb, const int32_t *__restrict__ trow, int pbeg, int pend, int t_first,
       int count, int stride, int r16, int g4, float &m_run, float &l_run, f32x4_t (&acc)[8],
       bool &bad) {
     const int64_t blk_bytes = static_cast<int64_t>(BS) * kRow * a.num_kv_heads;
@@ -494,10 +496,10 @@ struct Fast {
       for (int k = 0; k < kRing; ++k) {
         const int i = i0 + k;
         if (i < count) {
-          if (tpos(i) + kTile <= pend)
-            compute<false>(ring[k], qb, tpos(i), pend, g4, a.scale_log2, m_run, l_run, acc);
+          if (tpos(i) + kTile <= pend && tpos(i) >= pbeg)
+            compute<false>(ring[k], qb, tpos(i), pbeg, pend, g4, a.scale_log2, m_run, l_run, acc);
           else
-            compute<true>(ring[k], qb, tpos(i), pend, g4, a.scale_log2, m_run, l_run, acc);
+            compute<true>(ring[k], qb, tpos(i), pbeg, pend, g4, a.scale_log2, m_run, l_run, acc);
         }
         __builtin_amdgcn_sched_barrier(0);
         const int e = e_next;
@@ -579,13 +581,21 @@ struct Fast {
 
   // Position in the batch's tile list: sequence s (n positions, nts tiles
   // per unit, first global tile G), unit u (KV head * head groups + head
-  // group) and tile t of the unit.
+  // group) and tile t of the unit.  With a sliding window the unit's tiles
+  // start at tile t0 of the sequence (lo, the window's first position, lies
+  // in it); otherwise t0 = lo = 0.
   struct Cursor {
-    int s, n, nts, u, t;
+    int s, n, nts, u, t, t0, lo;
     int64_t G;
   };
-  static __device__ __forceinline__ int tiles_of(int n, int maxn) {
-    return (n > 0 && n <= maxn) ? (n + kTile - 1) / kTile : 0;
+  static __device__ __forceinline__ int tiles_of(int n, int maxn, int window) {
+    return (n > 0 && n <= maxn) ? (n + kTile - 1) / kTile - window_lo(n, window) / kTile : 0;
+  }
+  static __device__ __forceinline__ void set_seq(Cursor &c, int n, int maxn, int window) {
+    c.n = n;
+    c.nts = tiles_of(n, maxn, window);
+    c.lo = (n > 0 && n <= maxn) ? window_lo(n, window) : 0;
+    c.t0 = c.lo / kTile;
   }
   // next tile in list order (past the last one the cursor parks on s = S);
   // n_lane holds the first 64 sequences' lengths, one per lane
@@ -600,10 +610,10 @@ struct Fast {
       if (++c.s >= a.num_seqs) {
         c.n = 0;
         c.nts = 1;
+        c.t0 = c.lo = 0;
         return;
       }
-      c.n = c.s < 64 ? __builtin_amdgcn_readlane(n_lane, c.s) : load_const(a.ctx, c.s);
-      c.nts = tiles_of(c.n, maxn);
+      set_seq(c, c.s < 64 ? __builtin_amdgcn_readlane(n_lane, c.s) : load_const(a.ctx, c.s), maxn, a.window);
       if (c.nts > 0) return;
     }
   }
@@ -758,14 +768,14 @@ struct Fast {
     const int KVG = a.num_kv_heads * a.head_groups;
     const int maxn = a.max_blocks * BS;
     n_lane = lane < S ? a.ctx[lane] : 0;
-    cnt0 = tiles_of(n_lane, maxn);
+    cnt0 = tiles_of(n_lane, maxn, a.window);
     int64_t T;
     if (maxn < kScan32) {
       // 64 sequences' tiles fit 32 bits: a DPP scan
       incl0 = wave_incl_sum(static_cast<uint32_t>(cnt0));
       T = lane_value(incl0, 63);
       for (int c0 = 64; c0 < S; c0 += 64) {
-        const uint32_t cnt = (c0 + lane < S) ? static_cast<uint32_t>(tiles_of(a.ctx[c0 + lane], maxn)) : 0u;
+        const uint32_t cnt = (c0 + lane < S) ? static_cast<uint32_t>(tiles_of(a.ctx[c0 + lane], maxn, a.window)) : 0u;
         T += __builtin_amdgcn_readlane(wave_incl_sum(cnt), 63);
       }
     } else {
@@ -777,7 +787,7 @@ struct Fast {
       }
       T = lane_value(incl0, 63);
       for (int c0 = 64; c0 < S; c0 += 64) {
-        int64_t cnt = (c0 + lane < S) ? tiles_of(a.ctx[c0 + lane], maxn) : 0;
+        int64_t cnt = (c0 + lane < S) ? tiles_of(a.ctx[c0 + lane], maxn, a.window) : 0;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) cnt += __shfl_xor(cnt, o, 64);
         T += cnt;
@@ -803,7 +813,7 @@ struct Fast {
     } else {
       int64_t base = total0;
       for (int c0 = 64; c0 < S; c0 += 64) {
-        const int64_t t = (c0 + lane < S) ? tiles_of(a.ctx[c0 + lane], maxn) : 0;
+        const int64_t t = (c0 + lane < S) ? tiles_of(a.ctx[c0 + lane], maxn, a.window) : 0;
         int64_t incl;
         if (maxn < kScan32) {
           incl = wave_incl_sum(static_cast<uint32_t>(t));
@@ -830,8 +840,7 @@ struct Fast {
     }
     Cursor c;
     c.s = s;
-    c.n = n0;
-    c.nts = tiles_of(n0, maxn);
+    set_seq(c, n0, maxn, a.window);
     c.u = static_cast<int>(floor_div(g - G, c.nts));
     c.t = static_cast<int>(g - G - static_cast<int64_t>(c.u) * c.nts);
     c.G = G;
@@ -1049,7 +1058,7 @@ struct Fast {
     const uint8_t *kpool = static_cast<const uint8_t *>(a.k_pool);
     const uint8_t *vpool = static_cast<const uint8_t *>(a.v_pool);
     auto entry_at = [&](const Cursor &c) {
-      return load_const(a.tables + static_cast<int64_t>(c.s) * a.max_blocks, c.t * kTile / BS);
+      return load_const(a.tables + static_cast<int64_t>(c.s) * a.max_blocks, (c.t0 + c.t) * kTile / BS);
     };
     Cursor ci = c0;                    // issue cursor
     int64_t gi = lo;
@@ -1088,7 +1097,7 @@ struct Fast {
         const bool valid = static_cast<uint32_t>(e) < static_cast<uint32_t>(a.num_blocks);
         slot_bad = valid ? (slot_bad & ~(1u << k)) : (slot_bad | (1u << k));
         off = static_cast<int64_t>(valid ? e : 0) * blk_bytes + (ci.u / a.head_groups) * head_bytes +
-              (ci.t * kTile) % BS * kRow;
+              ((ci.t0 + ci.t) * kTile) % BS * kRow;
         on = valid;
         advance(a, ci, KVG, maxn, n_lane);
         if (gi + 1 < hi) e_next = entry_at(ci);
@@ -1147,11 +1156,11 @@ struct Fast {
             for (int e = 0; e < 8; ++e) acc[e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
             bad = false;
           }
-          const int tp = cc.t * kTile;
-          if (tp + kTile <= cc.n)
-            compute<false>(ring[k], qb, tp, cc.n, g4, a.scale_log2, m_run, l_run, acc);
+          const int tp = (cc.t0 + cc.t) * kTile;
+          if (tp + kTile <= cc.n && tp >= cc.lo)
+            compute<false>(ring[k], qb, tp, cc.lo, cc.n, g4, a.scale_log2, m_run, l_run, acc);
           else
-            compute<true>(ring[k], qb, tp, cc.n, g4, a.scale_log2, m_run, l_run, acc);
+            compute<true>(ring[k], qb, tp, cc.lo, cc.n, g4, a.scale_log2, m_run, l_run, acc);
           bad |= ((slot_bad >> k) & 1u) != 0;
 
           if (gc == hi - 1 || cc.t == cc.nts - 1) {
@@ -1456,8 +1465,8 @@ struct Fast {
   // Partitions the workgroups of the split take in turn: for each sequence
   // (in order), each of its units, each of its partitions; a sequence with
   // no positions or a bad length has one (that writes its rows).
-  static __device__ __forceinline__ int64_t seq_parts(int n, int maxn, int P) {
-    return (n <= 0 || n > maxn) ? 1 : (n + P - 1) / P;
+  static __device__ __forceinline__ int64_t seq_parts(int n, int maxn, int P, int window) {
+    return (n <= 0 || n > maxn) ? 1 : (n + P - 1) / P - window_lo(n, window) / P;
   }
 
   // The split with fixed partitions: gridDim.x workgroups take the batch's
@@ -1474,7 +1483,7 @@ struct Fast {
     int64_t incl = 0, cnt = 0;         // this lane's sequence c0 + lane: items up to and including it, its items
     auto scan = [&]() {
       const int s = c0 + lane;
-      cnt = s < S ? seq_parts(load_const(a.ctx, s), maxn, P) * KVG : 0;
+      cnt = s < S ? seq_parts(load_const(a.ctx, s), maxn, P, a.window) * KVG : 0;
       incl = cnt;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -1528,12 +1537,18 @@ struct Fast {
         store4(a, (row0 + (i >> 5)) * kHd + 4 * (i & 31), make_float4(fill, fill, fill, fill), 1.0f);
       return;
     }
+    // positions [pstart, pend) of partition `part`, counted from the one
+    // holding the first position of a sliding window; tiles start on
+    // multiples of 16, positions before pstart are masked
+    const int lo = window_lo(n, a.window);
     const int P = a.partition_size > 0 ? a.partition_size : n;
-    const int nparts = (n + P - 1) / P;
-    const int pstart = part * P;
-    if (pstart >= n) return;
-    const int pend = min(n, pstart + P);
-    const int ntiles = (pend - pstart + kTile - 1) / kTile;
+    const int nparts = (n + P - 1) / P - lo / P;
+    const int ap = lo / P + part;
+    if (ap * P >= n) return;
+    const int pstart = max(lo, ap * P);
+    const int pend = min(n, (ap + 1) * P);
+    const int tfirst = pstart / kTile;
+    const int ntiles = (pend + kTile - 1) / kTile - tfirst;
     const int nloc = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;   // this wave's tiles
 
     V8 qb[4];
@@ -1546,7 +1561,7 @@ struct Fast {
     bool bad = false;
     float m_run, l_run;
     f32x4_t acc[8];
-    accumulate(a, qb, kb, vb, trow, pend, pstart / kTile + wave, nloc, NW, r16, g4, m_run, l_run, acc,
+    accumulate(a, qb, kb, vb, trow, pstart, pend, tfirst + wave, nloc, NW, r16, g4, m_run, l_run, acc,
                bad);
 
     // add the four row groups' sums of exponentials, then hand the wave's
@@ -1623,7 +1638,7 @@ struct Fast {
     const int n = load_const(a.ctx, seq);
     if (n <= 0 || n > a.max_blocks * BS) return;
     const int P = a.partition_size;
-    const int nparts = (n + P - 1) / P;
+    const int nparts = (n + P - 1) / P - window_lo(n, a.window) / P;
     if (nparts <= 1) return;
     const int h = 2 * static_cast<int>(blockIdx.y) + (threadIdx.x >> 5);
     const int hcount = min(GT, a.group - hg * GT);

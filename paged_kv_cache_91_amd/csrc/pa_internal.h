@@ -43,6 +43,7 @@ struct DecodeArgs {
   float scale_log2;        // scale * k_scale * log2(e)
   float v_scale;           // 1 unless fp8
   int32_t wait_polls;      // balanced split: polls before a wait between waves of a workgroup gives up
+  int32_t window;          // sliding window: positions max(0, n - window) .. n-1 (0: the whole context)
 };
 
 // Polls (each about 30-80 ns) before a wait between the waves of one
@@ -68,12 +69,16 @@ struct WriteArgs {
 };
 
 struct CopyArgs {
-  void *k_pool;
-  void *v_pool;
-  const int64_t *pairs;
-  int64_t num_blocks;
+  const void *src_k;       // source pools (device, or pinned host memory's device address)
+  const void *src_v;
+  void *dst_k;             // destination pools (the source pools for a copy within one pool)
+  void *dst_v;
+  const int64_t *pairs;    // [num_pairs][2] (src block, dst block)
+  int64_t src_blocks;      // blocks in the source pools
+  int64_t dst_blocks;      // blocks in the destination pools
   int64_t block_bytes;     // Hkv * bs * D * element size
   int32_t num_pairs;
+  int32_t same_pool;       // 1: copy within one pool (pairs with src == dst are skipped)
 };
 
 // Each returns hipSuccess or the launch error; `supported` (when given) is
@@ -144,12 +149,13 @@ constexpr int kSlotMlFloats = 32;
 // Record `msg` for pa_last_error() on this thread; returns status.
 int set_error(int status, const char *msg);
 
-// The body of pa_decode (pa_api.cpp).  With clear_counters, the words of
+// The body of pa_decode and pa_decode_window (pa_api.cpp); window 0 is the
+// whole context.  With clear_counters, the words of
 // the workspace that must start at zero are zero-filled on the stream first
 // (after validation, so a failing call still enqueues nothing).
 int decode_entry(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
                  const pa_kv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
-                 const int32_t *context_lens, float scale, void *out, int32_t partition_size,
+                 const int32_t *context_lens, int32_t window, float scale, void *out, int32_t partition_size,
                  void *workspace, size_t workspace_bytes, pa_stream_t stream, bool clear_counters);
 
 // Workspace layout shared by the API layer and the kernels.

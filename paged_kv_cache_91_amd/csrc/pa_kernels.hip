@@ -83,9 +83,12 @@ struct DecodeKernel {
   // Issue the K/V loads of the wave tile starting at position `base`.
   // UNIFORM: every chunk of RPW positions lies inside one block (RPW <= bs),
   // so its table entry is wave-uniform.
+  // Positions outside [pbeg, pend) are read from the block of pbeg or
+  // pend - 1 instead (in bounds, and never a released block before a
+  // window) and masked by the caller.
   template <bool UNIFORM>
   static __device__ __forceinline__ void load_tile(
-      Tile &t, int base, int pend, int row, int col, const int32_t *__restrict__ trow,
+      Tile &t, int base, int pbeg, int pend, int row, int col, const int32_t *__restrict__ trow,
       const uint8_t *__restrict__ kbase, const uint8_t *__restrict__ vbase, int64_t block_bytes,
       int bs_log2, int64_t num_blocks, bool &bad) {
     const int bs_mask = (1 << bs_log2) - 1;
@@ -94,10 +97,10 @@ struct DecodeKernel {
       int j, off;
       if constexpr (UNIFORM) {
         const int c0 = base + c * RPW;
-        j = min(c0, pend - 1) >> bs_log2;
+        j = max(min(c0, pend - 1), pbeg) >> bs_log2;
         off = (c0 & bs_mask) + row;
       } else {
-        const int p = min(base + c * RPW + row, pend - 1);
+        const int p = max(min(base + c * RPW + row, pend - 1), pbeg);
         j = p >> bs_log2;
         off = p & bs_mask;
       }
@@ -125,11 +128,15 @@ struct DecodeKernel {
 
     const int n = a.ctx[seq];
     const bool bad_len = n < 0 || n > a.max_blocks * (1 << a.bs_log2);
-    int pstart = 0, pend = n;
+    // positions [pstart, pend); with a window, partitions are counted from
+    // the one holding the window's first position
+    const int lo = bad_len ? 0 : window_lo(n, a.window);
+    int pstart = lo, pend = n;
     if (a.partition_size > 0) {
-      pstart = part * a.partition_size;
-      pend = min(n, pstart + a.partition_size);
-      if (!bad_len && pstart >= n) return;        // partition past the context: no partial
+      const int ap = lo / a.partition_size + part;
+      pstart = max(lo, ap * a.partition_size);
+      pend = min(n, (ap + 1) * a.partition_size);
+      if (!bad_len && ap * a.partition_size >= n) return;   // partition past the context: no partial
     }
 
     // query heads handled here: hq0 .. hq0 + GT - 1, valid while h < hcount
@@ -185,16 +192,19 @@ struct DecodeKernel {
     const int32_t *trow = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
     bool bad = false;
 
-    const int ntiles = (pend - pstart + TP - 1) / TP;
+    // tiles start on a multiple of TP (so each load chunk stays inside one
+    // block); positions before pstart are masked
+    const int tstart = pstart & ~(TP - 1);
+    const int ntiles = (pend - tstart + TP - 1) / TP;
     Tile cur, nxt;
     if (wave < ntiles)
-      load_tile<UNIFORM>(cur, pstart + wave * TP, pend, row, col, trow, kbase, vbase, block_bytes,
+      load_tile<UNIFORM>(cur, tstart + wave * TP, pstart, pend, row, col, trow, kbase, vbase, block_bytes,
                          a.bs_log2, a.num_blocks, bad);
 
     for (int t = wave; t < ntiles; t += kDecodeWaves) {
-      const int base = pstart + t * TP;
+      const int base = tstart + t * TP;
       if (t + kDecodeWaves < ntiles)
-        load_tile<UNIFORM>(nxt, base + kDecodeWaves * TP, pend, row, col, trow, kbase, vbase,
+        load_tile<UNIFORM>(nxt, base + kDecodeWaves * TP, pstart, pend, row, col, trow, kbase, vbase,
                            block_bytes, a.bs_log2, a.num_blocks, bad);
 
       // scores of this tile: sc[c][h] for position base + c*RPW + row
@@ -203,7 +213,8 @@ struct DecodeKernel {
       for (int c = 0; c < CH; ++c) {
         float kf[E];
         KV::widen(cur.k[c], kf);
-        const bool valid = base + c * RPW + row < pend;
+        const int pos = base + c * RPW + row;
+        const bool valid = pos >= pstart && pos < pend;
 #pragma unroll
         for (int h = 0; h < GT; ++h) {
           float s = 0.0f;
@@ -240,7 +251,8 @@ struct DecodeKernel {
       for (int c = 0; c < CH; ++c) {
         float vf[E];
         KV::widen(cur.v[c], vf);
-        const bool valid = base + c * RPW + row < pend;
+        const int pos = base + c * RPW + row;
+        const bool valid = pos >= pstart && pos < pend;
 #pragma unroll
         for (int e = 0; e < E; ++e) vf[e] = valid ? vf[e] : 0.0f;
 #pragma unroll
@@ -325,7 +337,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeArgs a) {
     for (int d = threadIdx.x; d < D; d += blockDim.x) Qv<QS>::put(a.out, oi * D + d, __builtin_nanf(""));
     return;
   }
-  const int parts = (n + a.partition_size - 1) / a.partition_size;
+  const int parts = (n + a.partition_size - 1) / a.partition_size - window_lo(n, a.window) / a.partition_size;
   const float *pm = a.part_m + oi * a.max_parts;
   const float *pl = a.part_l + oi * a.max_parts;
   float big_m = -INFINITY;
@@ -448,17 +460,21 @@ __global__ __launch_bounds__(256) void write_fp8_kernel(WriteArgs a, int units_l
 // block copy
 // ---------------------------------------------------------------------------
 
+// Whole-block copies: within one pool (copy-on-write) or from one pool to
+// another of the same block shape (the swap between the GPU pool and pinned
+// host memory, whose loads or stores then cross the host link).
 // grid: (num_pairs, 2 [K, V], ceil(block_bytes / 4096)); 256 threads x 16 B.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
   const int pair = blockIdx.x;
   const int64_t src = a.pairs[2 * pair];
   const int64_t dst = a.pairs[2 * pair + 1];
-  if (src < 0 || dst < 0 || src >= a.num_blocks || dst >= a.num_blocks || src == dst) return;
-  uint8_t *pool = static_cast<uint8_t *>(blockIdx.y ? a.v_pool : a.k_pool);
+  if (src < 0 || dst < 0 || src >= a.src_blocks || dst >= a.dst_blocks || (a.same_pool && src == dst)) return;
+  const uint8_t *from = static_cast<const uint8_t *>(blockIdx.y ? a.src_v : a.src_k);
+  uint8_t *to = static_cast<uint8_t *>(blockIdx.y ? a.dst_v : a.dst_k);
   const int64_t off = static_cast<int64_t>(blockIdx.z) * 4096 + threadIdx.x * 16;
   if (off >= a.block_bytes) return;
-  *reinterpret_cast<uint4 *>(pool + dst * a.block_bytes + off) =
-      *reinterpret_cast<const uint4 *>(pool + src * a.block_bytes + off);
+  *reinterpret_cast<uint4 *>(to + dst * a.block_bytes + off) =
+      *reinterpret_cast<const uint4 *>(from + src * a.block_bytes + off);
 }
 
 // zero fill, 16 bytes a thread (a kernel rather than a memset node, so the

@@ -81,7 +81,7 @@ int pa_decode_noalloc(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t 
   // pa_decode's validation and kernels, with the scratch's counters zeroed
   // on the stream ahead of them (the scratch keeps the last call's contents)
   return pa_impl::decode_entry(q, q_dtype, num_seqs, num_q_heads, pool, block_tables, max_blocks_per_seq,
-                               context_lens, scale, out, partition_size, ws, ws_bytes, stream, true);
+                               context_lens, 0, scale, out, partition_size, ws, ws_bytes, stream, true);
 }
 
 }  // extern "C"

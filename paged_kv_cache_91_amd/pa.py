@@ -31,7 +31,8 @@ _ELEM = {PA_F32: 4, PA_F16: 2, PA_BF16: 2, PA_FP8_E4M3: 1}
 
 EXPORTED = ("pa_write_kv", "pa_decode", "pa_decode_workspace_bytes", "pa_copy_blocks",
             "pa_status_string", "pa_last_error", "pa_version", "pa_time_next_decode",
-            "pa_decode_status", "pa_set_wait_polls", "pa_decode_noalloc")
+            "pa_decode_status", "pa_set_wait_polls", "pa_decode_noalloc", "pa_swap_blocks",
+            "pa_decode_window")
 PA_NOALLOC_SCRATCH_BYTES = 32 << 20
 PA_WS_CLEAN, PA_WS_MISPLACED, PA_WS_TIMED_OUT = 0, 1, 2
 
@@ -96,6 +97,11 @@ def lib() -> ctypes.CDLL:
         L.pa_set_wait_polls.restype = ctypes.c_int
         L.pa_decode_noalloc.argtypes = [vp, i32, i32, i32, pool_p, vp, i32, vp, ctypes.c_float, vp, i32, vp]
         L.pa_decode_noalloc.restype = ctypes.c_int
+        L.pa_decode_window.argtypes = [vp, i32, i32, i32, pool_p, vp, i32, vp, i32, ctypes.c_float, vp, i32,
+                                       vp, ctypes.c_size_t, vp]
+        L.pa_decode_window.restype = ctypes.c_int
+        L.pa_swap_blocks.argtypes = [pool_p, pool_p, vp, i32, vp]
+        L.pa_swap_blocks.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -109,13 +115,13 @@ def _check(status: int, name: str) -> None:
         raise PaError(status, name, lib().pa_last_error().decode())
 
 
-def _ptr(t: Optional[torch.Tensor], what: str, allow_none=False) -> Optional[int]:
+def _ptr(t: Optional[torch.Tensor], what: str, allow_none=False, pinned_ok=False) -> Optional[int]:
     if t is None:
         if allow_none:
             return None
         raise ValueError(f"{what} is required")
-    if not t.is_cuda:
-        raise ValueError(f"{what} must be a device tensor")
+    if not t.is_cuda and not (pinned_ok and t.is_pinned()):
+        raise ValueError(f"{what} must be a device tensor" + (" or pinned host memory" if pinned_ok else ""))
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
     return t.data_ptr()
@@ -148,16 +154,17 @@ def dtype_code(t: torch.Tensor, dtype: Optional[str] = None) -> int:
 
 
 def make_pool(k_pool: torch.Tensor, v_pool: torch.Tensor, dtype: Optional[str] = None,
-              k_scale: float = 1.0, v_scale: float = 1.0) -> KvPool:
-    """Descriptor of caller-owned pools ``[num_blocks, Hkv, bs, D]``."""
+              k_scale: float = 1.0, v_scale: float = 1.0, host: bool = False) -> KvPool:
+    """Descriptor of caller-owned pools ``[num_blocks, Hkv, bs, D]``
+    (``host``: a swap area in pinned host memory, for pa_swap_blocks)."""
     if k_pool.shape != v_pool.shape or k_pool.dim() != 4:
         raise ValueError("pools must be 4-D [num_blocks, num_kv_heads, block_size, head_dim] of equal shape")
     code = dtype_code(k_pool, dtype)
     if dtype_code(v_pool, dtype) != code:
         raise ValueError("K and V pools differ in dtype")
     n, h, bs, d = k_pool.shape
-    return KvPool(_ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool"), n, h, bs, d, code,
-                  float(k_scale), float(v_scale))
+    return KvPool(_ptr(k_pool, "k_pool", pinned_ok=host), _ptr(v_pool, "v_pool", pinned_ok=host), n, h, bs, d,
+                  code, float(k_scale), float(v_scale))
 
 
 def pa_write_kv(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, pool: KvPool,
@@ -191,10 +198,21 @@ def new_workspace(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: 
     return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
 
 
+def pa_decode_window(q: torch.Tensor, pool: KvPool, block_tables: torch.Tensor,
+                     context_lens: torch.Tensor, window: int, scale: float,
+                     out: Optional[torch.Tensor] = None, partition_size: int = 0,
+                     workspace: Optional[torch.Tensor] = None, q_dtype: Optional[str] = None,
+                     stream=None) -> torch.Tensor:
+    """Paged decode under a sliding window of ``window`` positions (see
+    :func:`pa_decode` for the other arguments)."""
+    return pa_decode(q, pool, block_tables, context_lens, scale, out=out, partition_size=partition_size,
+                     workspace=workspace, q_dtype=q_dtype, stream=stream, _window=int(window))
+
+
 def pa_decode(q: torch.Tensor, pool: KvPool, block_tables: torch.Tensor,
               context_lens: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
               partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
-              q_dtype: Optional[str] = None, stream=None) -> torch.Tensor:
+              q_dtype: Optional[str] = None, stream=None, _window: Optional[int] = None) -> torch.Tensor:
     """Paged decode attention; returns ``out`` ([S, Hq, D], q's dtype).
 
     ``workspace`` (split mode) is allocated zero-filled here when not given,
@@ -223,10 +241,17 @@ def pa_decode(q: torch.Tensor, pool: KvPool, block_tables: torch.Tensor,
                 workspace = new_workspace(s, hq, pool.num_kv_heads, d, maxb, pool.block_size,
                                           partition_size, device=q.device)
         ws_ptr, ws_bytes = _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size()
-    _check(lib().pa_decode(_ptr(q, "q"), qcode, s, hq, ctypes.byref(pool), _ptr(block_tables, "block_tables"),
-                           maxb, _ptr(context_lens, "context_lens"), float(scale), _ptr(out, "out"),
-                           int(partition_size), ws_ptr, ws_bytes, _stream(stream)),
-           "pa_decode")
+    if _window is None:
+        _check(lib().pa_decode(_ptr(q, "q"), qcode, s, hq, ctypes.byref(pool), _ptr(block_tables, "block_tables"),
+                               maxb, _ptr(context_lens, "context_lens"), float(scale), _ptr(out, "out"),
+                               int(partition_size), ws_ptr, ws_bytes, _stream(stream)),
+               "pa_decode")
+    else:
+        _check(lib().pa_decode_window(_ptr(q, "q"), qcode, s, hq, ctypes.byref(pool),
+                                      _ptr(block_tables, "block_tables"), maxb, _ptr(context_lens, "context_lens"),
+                                      _window, float(scale), _ptr(out, "out"), int(partition_size), ws_ptr,
+                                      ws_bytes, _stream(stream)),
+               "pa_decode_window")
     if own_ws is not None:
         workspace.record_stream(own_ws)
     return out
@@ -260,6 +285,19 @@ def pa_copy_blocks(pool: KvPool, src_dst_pairs: torch.Tensor, stream=None) -> No
     _check(lib().pa_copy_blocks(ctypes.byref(pool), _ptr(src_dst_pairs, "src_dst_pairs") if num else None,
                                 num, _stream(stream)),
            "pa_copy_blocks")
+
+
+def pa_swap_blocks(src: KvPool, dst: KvPool, src_dst_pairs: torch.Tensor, stream=None) -> None:
+    """Copy whole blocks from pool pair ``src`` to ``dst`` (GPU pool and a
+    pinned host swap area, either way) for each (src, dst) row of an int64
+    ``[P, 2]`` tensor (device or pinned host)."""
+    if src_dst_pairs.dtype != torch.int64 or (src_dst_pairs.numel() and src_dst_pairs.shape[-1] != 2):
+        raise ValueError("src_dst_pairs must be int64 [num_pairs, 2]")
+    num = int(src_dst_pairs.numel() // 2)
+    _check(lib().pa_swap_blocks(ctypes.byref(src), ctypes.byref(dst),
+                                _ptr(src_dst_pairs, "src_dst_pairs", pinned_ok=True) if num else None, num,
+                                _stream(stream)),
+           "pa_swap_blocks")
 
 
 def pa_time_next_decode(start, stop) -> None:

@@ -226,7 +226,7 @@ def build_decode(seed: int, *, name: str, q_dtype: str, kv_dtype: str,
         num_blocks=num_blocks, q=q, k_pool=k_pool, v_pool=v_pool, block_tables=tables,
         context_lens=lens, scale=float(np.float32(1.0 / math.sqrt(head_dim))),
         partition_size=partition_size,
-        meta={"seed": seed, "alloc": alloc.stats(), "poison": poison, "pad_block": pad})
+        meta={"seed": seed, "alloc": alloc.stats(), "poison": poison, "pad_block": pad, "allocator": alloc})
 
 
 def relocate(wl: Workload, seed: int) -> Workload:

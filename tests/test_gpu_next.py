@@ -1,0 +1,217 @@
+"""GPU parity of the parts next to the decode hot path: sliding-window decode
+(pa_decode_window) and the GPU <-> pinned-host block swap (pa_swap_blocks).
+
+Window: every decode kernel (head-dim-128 single pass, fixed partitions, the
+balanced split; the generic kernels for other shapes) against the float64
+oracle with the same window, at the dtype's tolerance, with the table
+entries of blocks wholly before the window set to -1 and those blocks'
+contents poisoned with NaN (released blocks: never read).
+
+Swap: bit-exact against the oracle's block copy in both directions, decode
+through the swapped-in blocks bit-identical to decode before the swap, and
+pageable host memory refused on the host before any launch.
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_91_amd import pa
+from paged_kv_cache_91_amd import workloads as W
+from gpu_util import DEV, DeviceWorkload, dev_to_host, max_err, out_f64, say, to_dev, tol_for
+
+pytestmark = pytest.mark.gpu
+
+NAN = {"f32": np.float32(np.nan), "f16": np.float16(np.nan), "bf16": np.uint16(0x7FC0),
+       "fp8_e4m3": np.uint8(0x7F)}
+
+
+def _release_before_window(wl, window):
+    """Table entries of blocks wholly before each sequence's window become -1
+    and those blocks' contents NaN (as if freed and reused)."""
+    tables = wl.block_tables.copy()
+    kp, vp = wl.k_pool.copy(), wl.v_pool.copy()
+    bs = wl.block_size
+    for s, n in enumerate(wl.context_lens):
+        lo = oracle.window_start(int(n), window)
+        dead = tables[s, :lo // bs].copy()
+        if len(dead):
+            kp[dead] = NAN[wl.kv_dtype]
+            vp[dead] = NAN[wl.kv_dtype]
+            tables[s, :lo // bs] = -1
+    return tables, kp, vp
+
+
+def _check_window(wl, windows, parts):
+    for w in windows:
+        ref = oracle.oracle_decode(wl.q, wl.q_dtype, wl.k_pool, wl.v_pool, wl.kv_dtype, wl.block_tables,
+                                   wl.context_lens, wl.scale, wl.k_scale, wl.v_scale, window=w)
+        tables, kp, vp = _release_before_window(wl, w)
+        dev = DeviceWorkload(wl, tables=tables)
+        dev.k_pool, dev.v_pool = to_dev(kp, wl.kv_dtype), to_dev(vp, wl.kv_dtype)
+        dev.pool = pa.make_pool(dev.k_pool, dev.v_pool, dtype=wl.kv_dtype, k_scale=wl.k_scale,
+                                v_scale=wl.v_scale)
+        for p in parts:
+            out = torch.full_like(dev.q, float("nan"))
+            got = out_f64(pa.pa_decode_window(dev.q, dev.pool, dev.tables, dev.ctx, w, wl.scale, out=out,
+                                              partition_size=p, q_dtype=wl.q_dtype))
+            err = max_err(got, ref)
+            say(f"    window {w} partition {p}: max abs err {err:.3e}")
+            assert np.isfinite(got).all(), (w, p)
+            assert err <= tol_for(wl), (w, p, err)
+
+
+WINDOW_SHAPES = [
+    # (q_dtype, kv_dtype, Hq, Hkv, D, bs)
+    ("bf16", "bf16", 32, 8, 128, 16),
+    ("f16", "f16", 8, 8, 128, 32),
+    ("bf16", "bf16", 16, 2, 64, 8),        # generic kernels
+    ("f32", "f32", 4, 2, 8, 4),
+]
+
+
+@pytest.mark.parametrize("shape", WINDOW_SHAPES, ids=lambda s: "-".join(map(str, s)))
+def test_window_decode(shape):
+    qd, kd, hq, hkv, d, bs = shape
+    rng = np.random.default_rng(500 + d + bs)
+    lens = np.concatenate([[1, 15, 16, 17, 40, 255], rng.integers(300, 1500, size=4)])
+    need = sum(-(-int(n) // bs) for n in lens)
+    wl = W.build_decode(500 + d, name=f"win-{qd}", q_dtype=qd, kv_dtype=kd, num_q_heads=hq,
+                        num_kv_heads=hkv, head_dim=d, block_size=bs, num_blocks=need + 5,
+                        context_lens=lens, rng=rng)
+    say(f"[window] {shape}")
+    _check_window(wl, windows=(1, 16, 100, 517, 4096),
+                  parts=(0, bs * 4, 512 if 512 % bs == 0 else bs * 8, pa.PA_PARTITION_AUTO))
+
+
+def test_window_decode_fp8():
+    rng = np.random.default_rng(510)
+    lens = np.array([1, 31, 32, 33, 700, 2100, 5000])
+    need = sum(-(-int(n) // 32) for n in lens)
+    wl = W.build_write_filled(510, name="win-fp8", q_dtype="bf16", src_dtype="bf16", kv_dtype="fp8_e4m3",
+                              num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=32,
+                              num_blocks=need + 3, context_lens=lens, rng=rng)
+    kp, vp = oracle.oracle_write(wl.write_k, wl.write_v, wl.write_src_dtype, wl.slot_mapping, wl.k_pool,
+                                 wl.v_pool, wl.kv_dtype, wl.k_scale, wl.v_scale)
+    wl.k_pool, wl.v_pool = kp, vp
+    wl.write_k = wl.write_v = wl.slot_mapping = None
+    wl.meta = dict(wl.meta, filled_by_write=False)
+    say("[window] fp8")
+    _check_window(wl, windows=(33, 1000, 4096), parts=(0, 512, pa.PA_PARTITION_AUTO))
+
+
+def test_window_zero_is_plain_decode():
+    wl = W.config2(seed=520, num_seqs=6, ctx_range=(1, 900), num_blocks=400)
+    dev = DeviceWorkload(wl)
+    for p in (0, 64, pa.PA_PARTITION_AUTO):
+        a = dev.decode(partition_size=p).cpu()
+        b = pa.pa_decode_window(dev.q, dev.pool, dev.tables, dev.ctx, 0, wl.scale,
+                                out=torch.full_like(dev.q, float("nan")), partition_size=p).cpu()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), p
+
+
+# ---------------------------------------------------------------------------
+# swap
+# ---------------------------------------------------------------------------
+
+def _pinned_like(shape, dtype):
+    return torch.zeros(shape, dtype=dtype, pin_memory=True)
+
+
+def test_swap_round_trip_and_decode():
+    """The allocator swaps two sequences out (every block, to pinned host
+    slots), their GPU blocks are reused and scribbled over, then they are
+    swapped back into other GPU blocks: bit-exact both ways, and decode
+    through the new tables is bit-identical to decode before the swap."""
+    wl = W.config2(seed=530, num_seqs=5, ctx_range=(20, 700), num_blocks=260)
+    dev = DeviceWorkload(wl)
+    before = dev.decode(partition_size=pa.PA_PARTITION_AUTO).cpu()
+    bs = wl.block_size
+    alloc = wl.meta["allocator"]            # the allocator that built the tables
+    alloc.add_host_area(128)
+    alloc.check()
+    hk = _pinned_like(dev.k_pool.shape[:0] + (128,) + tuple(dev.k_pool.shape[1:]), dev.k_pool.dtype)
+    hv = torch.zeros_like(hk).pin_memory()
+    host = pa.make_pool(hk, hv, host=True)
+    out_pairs = []
+    for s in (1, 3):
+        pairs = np.array(alloc.swap_out(s), dtype=np.int64).reshape(-1, 2)
+        out_pairs.append(pairs)
+        pa.pa_swap_blocks(dev.pool, host, torch.from_numpy(pairs).to(DEV))
+    torch.cuda.synchronize()
+    kp_host, vp_host = dev.pools_host()
+    for pairs in out_pairs:
+        rk, rv = oracle.oracle_swap(kp_host, vp_host, dev_to_host(hk, "bf16") * 0, dev_to_host(hv, "bf16") * 0,
+                                    pairs)
+        assert np.array_equal(dev_to_host(hk, "bf16")[pairs[:, 1]], rk[pairs[:, 1]])
+        assert np.array_equal(dev_to_host(hv, "bf16")[pairs[:, 1]], rv[pairs[:, 1]])
+    # the freed GPU blocks are handed out again and overwritten
+    freed = np.concatenate([p[:, 0] for p in out_pairs])
+    dev.k_pool[torch.from_numpy(freed).to(DEV)] = float("nan")
+    dev.v_pool[torch.from_numpy(freed).to(DEV)] = float("nan")
+    alloc.add_sequence(99, len(freed) * bs)
+    new_tables = wl.block_tables.copy()
+    for s in (1, 3):
+        pairs = np.array(alloc.swap_in(s), dtype=np.int64).reshape(-1, 2)
+        pa.pa_swap_blocks(host, dev.pool, torch.from_numpy(pairs).pin_memory())    # pairs in pinned memory
+        new_tables[s, :len(pairs)] = alloc.block_table(s)
+    alloc.check()
+    dev.set_tables(new_tables)
+    after = dev.decode(partition_size=pa.PA_PARTITION_AUTO).cpu()
+    assert torch.equal(before.view(torch.int16), after.view(torch.int16))
+    ref = oracle.oracle_decode(wl.q, wl.q_dtype, wl.k_pool, wl.v_pool, wl.kv_dtype, wl.block_tables,
+                               wl.context_lens, wl.scale)
+    assert max_err(out_f64(after), ref) <= 2e-2
+
+
+@pytest.mark.parametrize("dtype", ["f16", "fp8_e4m3"])
+def test_swap_bitexact_against_oracle(dtype):
+    rng = np.random.default_rng(540)
+    shape = (40, 4, 16, 128)
+    if dtype == "f16":
+        src = rng.standard_normal(shape).astype(np.float16)
+        tdt = torch.float16
+    else:
+        src = rng.integers(0, 256, size=shape, dtype=np.uint8)
+        tdt = torch.uint8
+    ks, vs = torch.from_numpy(src).to(DEV), torch.from_numpy(src[::-1].copy()).to(DEV)
+    hk = torch.zeros((24,) + shape[1:], dtype=tdt).pin_memory()
+    hv = torch.zeros_like(hk).pin_memory()
+    kwargs = dict(dtype=dtype, k_scale=0.5, v_scale=0.25) if dtype == "fp8_e4m3" else {}
+    gpu = pa.make_pool(ks, vs, **kwargs)
+    host = pa.make_pool(hk, hv, host=True, **kwargs)
+    pairs = np.stack([rng.permutation(40)[:20], rng.permutation(24)[:20]], 1).astype(np.int64)
+    pa.pa_swap_blocks(gpu, host, torch.from_numpy(pairs).to(DEV))
+    torch.cuda.synchronize()
+    rk, rv = oracle.oracle_swap(src, src[::-1].copy(), np.zeros((24,) + shape[1:], src.dtype),
+                                np.zeros((24,) + shape[1:], src.dtype), pairs)
+    assert np.array_equal(hk.numpy(), rk) and np.array_equal(hv.numpy(), rv)
+    # and back, to other GPU blocks of a second pool
+    k2, v2 = torch.zeros_like(ks), torch.zeros_like(vs)
+    back = np.stack([pairs[:, 1], np.arange(20)], 1).astype(np.int64)
+    pa.pa_swap_blocks(host, pa.make_pool(k2, v2, **kwargs), torch.from_numpy(back).to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(k2[:20].cpu(), ks[torch.from_numpy(pairs[:, 0]).to(DEV)].cpu())
+    assert torch.equal(v2[:20].cpu(), vs[torch.from_numpy(pairs[:, 0]).to(DEV)].cpu())
+    assert not k2[20:].any()
+
+
+def test_swap_refuses_pageable_host_memory():
+    """A host pool in ordinary (pageable) memory is refused on the host:
+    PA_ERR_INVALID_ARG, nothing launched, the device pool untouched."""
+    ks = torch.ones((8, 2, 16, 64), dtype=torch.float16, device=DEV)
+    vs = torch.ones_like(ks)
+    pageable = np.zeros((8, 2, 16, 64), np.float16)
+    pageable_v = np.zeros_like(pageable)
+    bad = pa.KvPool(pageable.ctypes.data, pageable_v.ctypes.data, 8, 2, 16, 64, pa.PA_F16, 1.0, 1.0)
+    gpu = pa.make_pool(ks, vs)
+    pairs = torch.tensor([[0, 1]], dtype=torch.int64, device=DEV)
+    st = pa.lib().pa_swap_blocks(ctypes.byref(gpu), ctypes.byref(bad), pairs.data_ptr(), 1, None)
+    assert st == -1
+    assert b"pinned" in pa.lib().pa_last_error()
+    torch.cuda.synchronize()
+    assert not pageable.any()
+    assert bool((ks == 1).all())
