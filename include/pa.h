@@ -221,6 +221,45 @@ int pa_decode_window(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t n
                      int32_t partition_size, void *workspace, size_t workspace_bytes, pa_stream_t stream);
 
 /*
+ * pa_prefill -- causal multi-query attention over the paged cache: a prompt,
+ * or a chunk of one after a cached prefix (chunked prefill).  zerocoder.ru
+ * "Что такое PagedAttention", section "Зачем KV cache вообще нужен" (in
+ * causal attention each position uses the keys and values of the positions
+ * before it); ultralytics.com "PagedAttention", section "관련 기법" (engines run
+ * FlashAttention-style kernels that read those from the paged blocks).
+ *
+ * Sequence s < num_seqs holds n = context_lens[s] positions in its blocks,
+ * the new ones already written (pa_write_kv).  Its L = query_start[s+1] -
+ * query_start[s] queries are rows query_start[s] .. query_start[s+1]-1 of q
+ * and stand for its last L positions: row query_start[s] + i is position
+ * p = n - L + i and attends positions lo .. p (lo = 0, or max(0, p + 1 -
+ * window) under a sliding window), for every query head h with KV head
+ * h / (num_q_heads / num_kv_heads):
+ *     out[row][h][:] = sum_{lo <= j <= p} softmax_j(scale * <q[row][h], K_j>) V_j
+ * with float32 accumulation; out is rounded to nearest even in q's dtype.
+ * The last query of a sequence computes exactly the decode step of
+ * pa_decode.  Table entries of blocks holding no position some query of the
+ * sequence attends are never read.
+ *
+ *   q, out        device, [num_tokens][num_q_heads][head_dim] of q_dtype; out
+ *                 must not overlap q.  Rows of sequences with invalid
+ *                 lengths (n outside [0, max_blocks_per_seq * bs], L > n) are
+ *                 NaN.
+ *   query_start   device, int32 [num_seqs + 1], nondecreasing, query_start[0]
+ *                 = 0 and query_start[num_seqs] = num_tokens.
+ *   window        >= 0; 0 attends every earlier position.
+ * q_dtype / pool dtype combinations, head dims, block sizes, block_tables,
+ * context_lens and scale are as for pa_decode.  No workspace is needed.
+ * Head dim 128 with a bf16 or f16 cache of block size 16 or 32 and 1, 2, 4
+ * or 8 query heads per KV head runs on the matrix cores; other shapes run a
+ * vector kernel (one workgroup per query row and head group).
+ */
+int pa_prefill(const void *q, int32_t q_dtype, int32_t num_tokens, int32_t num_q_heads,
+               const pa_kv_pool *pool, int32_t num_seqs, const int32_t *block_tables,
+               int32_t max_blocks_per_seq, const int32_t *context_lens, const int32_t *query_start,
+               int32_t window, float scale, void *out, pa_stream_t stream);
+
+/*
  * pa_copy_blocks -- copy-on-write block copy.
  *
  * For each pair i < num_pairs, (src, dst) = (src_dst_pairs[2i], src_dst_pairs[2i+1]):

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libpa.so")
 # (source, extra defines) per object; the head-dim-128 decode file is built
 # once per (q, cache) dtype pair so the pairs compile in parallel
-UNITS = [("pa_kernels.hip", []), ("pa_api.cpp", []), ("pa_noalloc.hip", [])] + [
+UNITS = [("pa_kernels.hip", []), ("pa_api.cpp", []), ("pa_noalloc.hip", []), ("pa_prefill.hip", [])] + [
     ("pa_decode_fast.hip", [f"-DPA_FAST_COMBO={i}"]) for i in range(4)]
 SOURCES = sorted({os.path.join(PKG, "csrc", f) for f, _ in UNITS})
 ARCH = "gfx950"

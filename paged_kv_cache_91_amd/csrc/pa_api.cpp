@@ -418,6 +418,75 @@ int pa_copy_blocks(const pa_kv_pool *pool, const int64_t *src_dst_pairs, int32_t
   return ok();
 }
 
+int pa_prefill(const void *q, int32_t q_dtype, int32_t num_tokens, int32_t num_q_heads,
+               const pa_kv_pool *pool, int32_t num_seqs, const int32_t *block_tables,
+               int32_t max_blocks_per_seq, const int32_t *context_lens, const int32_t *query_start,
+               int32_t window, float scale, void *out, pa_stream_t stream) {
+  if (int st = check_pool(pool)) return st;
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens must be >= 0");
+  if (num_tokens == 0) return ok();
+  if (num_seqs <= 0 || num_seqs > 65535) return fail(PA_ERR_INVALID_ARG, "num_seqs must be in [1, 65535]");
+  if (!q || !out || !block_tables || !context_lens || !query_start)
+    return fail(PA_ERR_INVALID_ARG, "q, out, block_tables, context_lens or query_start is NULL");
+  if (q == out) return fail(PA_ERR_INVALID_ARG, "out must not alias q");
+  if (num_q_heads <= 0 || num_q_heads % pool->num_kv_heads)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                num_q_heads, pool->num_kv_heads);
+  if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
+  if (static_cast<int64_t>(max_blocks_per_seq) * pool->block_size > 0x7fffffffLL)
+    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq * block_size overflows int32");
+  if (window < 0) return fail(PA_ERR_INVALID_ARG, "window must be >= 0");
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+  if (q_dtype != PA_F32 && q_dtype != PA_F16 && q_dtype != PA_BF16)
+    return fail(PA_ERR_INVALID_ARG, "q dtype must be F32, F16 or BF16");
+  const bool combo = (q_dtype == pool->dtype) ||
+                     (pool->dtype == PA_FP8_E4M3 && (q_dtype == PA_BF16 || q_dtype == PA_F16));
+  if (!combo) return fail(PA_ERR_UNSUPPORTED, "q dtype %d with pool dtype %d not built", q_dtype, pool->dtype);
+  const int group = num_q_heads / pool->num_kv_heads;
+  const int hpw = heads_per_wg(group);
+  const int head_groups = static_cast<int>(ceil_div(group, hpw));
+  if (static_cast<int64_t>(pool->num_kv_heads) * head_groups > 65535)
+    return fail(PA_ERR_INVALID_ARG, "too many heads");
+
+  pa_impl::DecodeArgs a{};
+  a.q = q;
+  a.k_pool = pool->k_pool;
+  a.v_pool = pool->v_pool;
+  a.tables = block_tables;
+  a.ctx = context_lens;
+  a.out = out;
+  a.num_blocks = pool->num_blocks;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.group = group;
+  a.heads_per_wg = hpw;
+  a.head_groups = head_groups;
+  a.head_dim = pool->head_dim;
+  a.block_size = pool->block_size;
+  a.bs_log2 = log2_exact(pool->block_size);
+  a.max_blocks = max_blocks_per_seq;
+  a.partition_size = 0;
+  a.max_parts = 1;
+  const double ks = pool->dtype == PA_FP8_E4M3 ? static_cast<double>(pool->k_scale) : 1.0;
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * ks * 1.4426950408889634);
+  a.v_scale = pool->dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
+  a.window = window;
+  a.query_start = query_start;
+  a.num_tokens = num_tokens;
+  const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (pa_impl::prefill_fast_applies(q_dtype, pool->dtype, a)) {
+    e = pa_impl::launch_prefill_fast(q_dtype, a, hs);
+  } else {
+    bool supported = true;
+    e = pa_impl::launch_decode(q_dtype, pool->dtype, a, hs, &supported);
+    if (!supported) return fail(PA_ERR_UNSUPPORTED, "prefill specialisation not built");
+  }
+  if (e != hipSuccess) return hip_fail(e);
+  return ok();
+}
+
 // Device address a kernel of the current device can use for `p`: device
 // memory of the current device as is, pinned host memory through its mapped
 // device address; anything else (pageable host memory, another device's

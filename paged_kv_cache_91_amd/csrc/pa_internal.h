@@ -44,6 +44,11 @@ struct DecodeArgs {
   float v_scale;           // 1 unless fp8
   int32_t wait_polls;      // balanced split: polls before a wait between waves of a workgroup gives up
   int32_t window;          // sliding window: positions max(0, n - window) .. n-1 (0: the whole context)
+  // prefill (causal, several queries per sequence): non-null query_start
+  // [S + 1] gives sequence s the q / out rows query_start[s] .. query_start[s+1]-1,
+  // which stand for its last positions; num_tokens = query_start[S]
+  const int32_t *query_start;
+  int32_t num_tokens;
 };
 
 // Polls (each about 30-80 ns) before a wait between the waves of one
@@ -117,6 +122,12 @@ inline hipError_t launch_decode_fast(int q_dtype, int kv_dtype, const DecodeArgs
   if (q_dtype == kF16 && kv_dtype == kFP8) return launch_fast_f16_fp8(a, s, ev);
   return hipErrorInvalidValue;
 }
+
+// Prefill (pa_prefill.hip): the matrix-core kernel for head_dim 128, block
+// 16/32, 16-bit caches and groups 1, 2, 4, 8; prefill_fast_applies() says
+// whether it covers a call (else the generic kernel's prefill mode runs).
+bool prefill_fast_applies(int q_dtype, int kv_dtype, const DecodeArgs &a);
+hipError_t launch_prefill_fast(int q_dtype, const DecodeArgs &a, hipStream_t s);
 
 // Compute units of the current device (256 when it cannot be queried, e.g.
 // on a machine without a GPU, where only sizes are computed).

@@ -62,6 +62,21 @@ __device__ __forceinline__ float xor_max(float v) {
 
 constexpr int kDecodeWaves = 4;
 
+// The sequence whose query rows hold packed row t: the last s with
+// query_start[s] <= t (query_start is nondecreasing, so those s form a
+// prefix), found 64 sequences per wave-wide load.
+__device__ __forceinline__ int seq_of_row(const DecodeArgs &a, int t, int lane) {
+  int count = 0;
+  for (int c0 = 0; c0 < a.num_seqs; c0 += kWave) {
+    const int s = c0 + lane;
+    const bool le = s < a.num_seqs && a.query_start[s] <= t;
+    const int k = __popcll(__ballot(le));
+    count += k;
+    if (k < kWave) break;
+  }
+  return count - 1;
+}
+
 template <typename QS, typename KS, int D, int GT>
 struct DecodeKernel {
   using KV = Kv<KS>;
@@ -117,17 +132,39 @@ struct DecodeKernel {
 
   template <bool UNIFORM>
   static __device__ void run(const DecodeArgs &a) {
-    const int part = blockIdx.x;
     const int kvh = blockIdx.y / a.head_groups;
     const int hg = blockIdx.y - kvh * a.head_groups;
-    const int seq = blockIdx.z;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x >> 6;
     const int row = lane / LPR;
     const int col = lane % LPR;
+    const int maxn = a.max_blocks * (1 << a.bs_log2);
 
-    const int n = a.ctx[seq];
-    const bool bad_len = n < 0 || n > a.max_blocks * (1 << a.bs_log2);
+    // decode: sequence blockIdx.z, partition blockIdx.x, its q / out row;
+    // prefill: q / out row blockIdx.x of sequence `seq`, attending its
+    // positions 0 .. p (n = p + 1)
+    int part, seq, n;
+    int64_t qrow;
+    bool bad_len;
+    if (a.query_start) {
+      const int t = blockIdx.x;
+      seq = max(seq_of_row(a, t, lane), 0);
+      const int ns = a.ctx[seq];
+      const int q0 = a.query_start[seq];
+      const int L = a.query_start[seq + 1] - q0;
+      // a malformed prefix sum (row outside its sequence's range) or length
+      // gives NaN rows
+      bad_len = ns < 0 || ns > maxn || L > ns || t < q0 || t >= q0 + L;
+      n = bad_len ? 0 : ns - L + (t - q0) + 1;
+      part = 0;
+      qrow = t;
+    } else {
+      part = blockIdx.x;
+      seq = blockIdx.z;
+      n = a.ctx[seq];
+      bad_len = n < 0 || n > maxn;
+      qrow = seq;
+    }
     // positions [pstart, pend); with a window, partitions are counted from
     // the one holding the window's first position
     const int lo = bad_len ? 0 : window_lo(n, a.window);
@@ -153,7 +190,7 @@ struct DecodeKernel {
       for (int i = threadIdx.x; i < GT * D; i += kDecodeWaves * kWave) {
         const int h = i / D, d = i % D;
         if (h >= hcount) continue;
-        const int64_t oi = (static_cast<int64_t>(seq) * a.num_q_heads + hq0 + h);
+        const int64_t oi = (qrow * a.num_q_heads + hq0 + h);
         if (a.partition_size > 0) {
           if (d == 0) { a.part_m[oi * a.max_parts + part] = fill; a.part_l[oi * a.max_parts + part] = fill; }
           a.part_o[(oi * a.max_parts + part) * D + d] = fill;
@@ -171,7 +208,7 @@ struct DecodeKernel {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         q[h][e] = (h < hcount)
-            ? Qv<QS>::get(a.q, (static_cast<int64_t>(seq) * a.num_q_heads + hq0 + h) * D + col * E + e)
+            ? Qv<QS>::get(a.q, (qrow * a.num_q_heads + hq0 + h) * D + col * E + e)
             : 0.0f;
       }
     }
@@ -301,7 +338,7 @@ struct DecodeKernel {
         l = fmaf(s_l[w][h], f, l);
         o = fmaf(s_acc[w][h][d], f, o);
       }
-      const int64_t oi = static_cast<int64_t>(seq) * a.num_q_heads + hq0 + h;
+      const int64_t oi = qrow * a.num_q_heads + hq0 + h;
       if (a.partition_size > 0) {
         const float nanv = __builtin_nanf("");
         if (d == 0) {
@@ -358,7 +395,8 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeArgs a) {
 
 template <typename QS, typename KS, int D>
 hipError_t launch_decode_d(const DecodeArgs &a, hipStream_t s) {
-  const dim3 grid(a.partition_size > 0 ? a.max_parts : 1, a.num_kv_heads * a.head_groups, a.num_seqs);
+  const dim3 grid(a.query_start ? a.num_tokens : (a.partition_size > 0 ? a.max_parts : 1),
+                  a.num_kv_heads * a.head_groups, a.query_start ? 1 : a.num_seqs);
   const dim3 block(kDecodeWaves * kWave);
   switch (a.heads_per_wg) {
     case 1: hipLaunchKernelGGL((decode_kernel<QS, KS, D, 1>), grid, block, 0, s, a); break;

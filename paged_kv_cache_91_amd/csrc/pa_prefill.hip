@@ -1,0 +1,378 @@
+// Paged prefill for head_dim 128 on gfx950: causal multi-query attention of
+// a prompt (or a chunk of one after a cached prefix) over K/V read through
+// the block table, with both products on the matrix cores.
+//
+// What is computed is the causal attention of zerocoder.ru "Что такое
+// PagedAttention", section "Зачем KV cache вообще нужен" (each position
+// attends the keys and values of the positions before it), read from the
+// paged blocks as ultralytics.com "PagedAttention", section "관련 기법",
+// describes for FlashAttention-style kernels: K/V tiles are streamed through
+// on-chip memory and the softmax is evaluated online, so the score matrix
+// never reaches HBM.
+//
+// Work.  A workgroup of 4 waves owns one (sequence, KV head) and a block of
+// kQb consecutive query positions; its columns are the (position, query
+// head) pairs of the group (16 per column group, head fastest), 2 column
+// groups per wave.  Keys are walked from the first one any column sees to
+// the block's last position in tiles of 32, each staged once in LDS for all
+// four waves (padded rows; double-buffered, the next tile's global loads in
+// flight during the current tile's compute).
+//
+// Per 16-key half of a tile and column group (the decode kernel's layout with
+// query columns in place of heads):
+//   S^T = K . Q^T   four v_mfma_f32_16x16x32 (A = 16 key rows from LDS,
+//                   B = the column group's q), lane l holds keys 4*(l/16)+r
+//                   of column l%16;
+//   online softmax per column in the base-2 domain, causal (and window) mask
+//   only on tiles that reach past a column's position;
+//   O^T += V^T . P  eight v_mfma_f32_16x16x16 (A = V rows from LDS repacked
+//                   with v_perm, B = the probabilities in place).
+// Blocks are ordered so that all blocks of one (sequence, KV head) land on
+// one XCD (their K/V is re-read from that XCD's L2), last block first.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "pa_common.h"
+#include "pa_internal.h"
+#include "pa_mfma.h"
+
+namespace pa_impl {
+namespace {
+
+constexpr int kHd = 128;
+constexpr int kKeys = 32;                  // keys per staged tile
+constexpr int kRowBytes = kHd * 2 + 16;    // LDS row stride: 16 lanes reading one column of 16 rows spread over the banks
+constexpr int kWaves = 4;
+constexpr int kCg = 2;                     // column groups (16 columns each) per wave
+
+typedef const __attribute__((address_space(4))) int32_t cint32_t;
+__device__ __forceinline__ int load_const(const int32_t *p, int64_t i) { return ((cint32_t *)p)[i]; }
+
+template <typename QS, int G, int BS>
+struct Prefill {
+  using M = Mma<QS>;
+  using V8 = typename M::V8;
+  using V4 = typename M::V4;
+  static constexpr int kPos = 16 / G;                   // positions per column group
+  static constexpr int kQb = kWaves * kCg * kPos;       // query positions per workgroup
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group must divide 16");
+  static_assert(BS == 16 || BS == 32, "block size 16 or 32");
+
+  // head dims of lane group g4's 8-element run in MFMA j (A and B agree)
+  static __device__ __forceinline__ int dbase(int j, int g4) { return 32 * j + 8 * g4; }
+
+  static __device__ __forceinline__ void store4(void *out, int64_t idx, float4 o, float mul) {
+    uint2 w;
+    if constexpr (std::is_same<QS, BF16S>::value) {
+      w.x = f32_to_bf16(o.x * mul) | (static_cast<uint32_t>(f32_to_bf16(o.y * mul)) << 16);
+      w.y = f32_to_bf16(o.z * mul) | (static_cast<uint32_t>(f32_to_bf16(o.w * mul)) << 16);
+    } else {
+      w.x = f32_to_f16(o.x * mul) | (static_cast<uint32_t>(f32_to_f16(o.y * mul)) << 16);
+      w.y = f32_to_f16(o.z * mul) | (static_cast<uint32_t>(f32_to_f16(o.w * mul)) << 16);
+    }
+    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + idx) = w;
+  }
+
+  static __device__ void run(const DecodeArgs &a) {
+    __shared__ __align__(16) uint8_t s_k[2][kKeys * kRowBytes];
+    __shared__ __align__(16) uint8_t s_v[2][kKeys * kRowBytes];
+    const int tid = threadIdx.x;
+    const int wave = uniform(static_cast<int>(tid >> 6));
+    const int lane = tid & 63;
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int S = a.num_seqs;
+    const int Hkv = a.num_kv_heads;
+    const int maxn = a.max_blocks * BS;
+
+    // item -> (KV head, block r of the batch's query blocks); blocks are
+    // counted per sequence, ceil(L / kQb) each, found by a wave-wide scan
+    const int64_t item = blockIdx.x;
+    const int kvh = static_cast<int>(item % Hkv);
+    const int64_t r = item / Hkv;
+    int seq = -1, nb_s = 0;
+    int64_t k_in = 0;
+    {
+      int64_t base = 0;
+      for (int c0 = 0; c0 < S; c0 += 64) {
+        const int s = c0 + lane;
+        uint32_t nb = 0;
+        if (s < S) {
+          const int L = a.query_start[s + 1] - a.query_start[s];
+          nb = L > 0 ? static_cast<uint32_t>((L + kQb - 1) / kQb) : 0u;
+        }
+        const uint32_t incl = wave_incl_sum(nb);
+        const int64_t total = __builtin_amdgcn_readlane(incl, 63);
+        if (base + total > r) {
+          const uint64_t m = __builtin_amdgcn_ballot_w64(base + static_cast<int64_t>(incl) > r);
+          const int first = uniform(static_cast<int>(__builtin_ctzll(m)));
+          seq = c0 + first;
+          nb_s = static_cast<int>(__builtin_amdgcn_readlane(nb, first));
+          k_in = r - (base + static_cast<int64_t>(__builtin_amdgcn_readlane(incl, first)) - nb_s);
+          break;
+        }
+        base += total;
+      }
+    }
+    if (seq < 0) return;                        // past the batch's blocks (the grid is an upper bound)
+
+    const int q0 = load_const(a.query_start, seq);
+    const int L = load_const(a.query_start, seq + 1) - q0;
+    const int n = load_const(a.ctx, seq);
+    const int qb = nb_s - 1 - static_cast<int>(k_in);          // last block first
+    const int P0 = n - L;                                       // the first query's position
+    const int pb0 = P0 + qb * kQb;                              // this block's first query position
+    const int pb1 = min(n, pb0 + kQb);                          // one past its last
+    const bool bad_len = n < 0 || n > maxn || L > n;
+
+    // this lane's column in each column group: position qp[cg], head h
+    const int h = kvh * G + r16 % G;
+    int qp[kCg];
+    bool valid[kCg];
+#pragma unroll
+    for (int cg = 0; cg < kCg; ++cg) {
+      qp[cg] = pb0 + (wave * kCg + cg) * kPos + r16 / G;
+      valid[cg] = qp[cg] < pb1;
+    }
+    auto out_idx = [&](int cg) {
+      return (static_cast<int64_t>(q0 + qp[cg] - P0) * a.num_q_heads + h) * kHd + 32 * g4;
+    };
+    if (bad_len) {
+      const float nanv = __builtin_nanf("");
+#pragma unroll
+      for (int cg = 0; cg < kCg; ++cg)
+        if (valid[cg] && qp[cg] >= pb0)
+#pragma unroll
+          for (int r4 = 0; r4 < 8; ++r4) store4(a.out, out_idx(cg) + 4 * r4, make_float4(nanv, nanv, nanv, nanv), 1.0f);
+      return;
+    }
+
+    // q of each column as the MFMA B operand (zero for columns past the block)
+    V8 qop[kCg][4];
+#pragma unroll
+    for (int cg = 0; cg < kCg; ++cg) {
+      const uint16_t *qrow = static_cast<const uint16_t *>(a.q) +
+                             (static_cast<int64_t>(q0 + qp[cg] - P0) * a.num_q_heads + h) * kHd;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint4 w = make_uint4(0u, 0u, 0u, 0u);
+        if (valid[cg]) w = *reinterpret_cast<const uint4 *>(qrow + dbase(j, g4));
+        qop[cg][j] = __builtin_bit_cast(V8, w);
+      }
+    }
+
+    // keys [klo, khi): from the first position any column sees to the last
+    // query's position
+    const int khi = pb1;
+    const int klo = window_lo(pb0 + 1, a.window);
+    const int kt0 = klo / kKeys;
+    const int ntiles = (khi + kKeys - 1) / kKeys - kt0;
+    // this wave's columns: positions wq0 .. wq1 (none when wq0 >= pb1)
+    const int wq0 = pb0 + wave * kCg * kPos;
+    const int wq1 = min(pb1 - 1, wq0 + kCg * kPos - 1);
+    const bool idle = wq0 >= pb1;
+    const int wlo0 = window_lo(wq0 + 1, a.window);              // smallest first key of the wave's columns
+    const int wlo1 = window_lo(wq1 + 1, a.window);              // largest
+    int lo_col[kCg];
+#pragma unroll
+    for (int cg = 0; cg < kCg; ++cg) lo_col[cg] = window_lo(qp[cg] + 1, a.window);
+
+    // staging: thread (row rr, 16-byte chunk ch) moves rows rr and rr + 16
+    // of K and of V; table entries are clamped to [klo, khi)'s blocks so
+    // released or unwritten entries are never read
+    const int rr = tid >> 4, ch = tid & 15;
+    const int64_t head_bytes = static_cast<int64_t>(BS) * kHd * 2;
+    const int64_t blk_bytes = head_bytes * Hkv;
+    const uint8_t *kpool = static_cast<const uint8_t *>(a.k_pool) + kvh * head_bytes;
+    const uint8_t *vpool = static_cast<const uint8_t *>(a.v_pool) + kvh * head_bytes;
+    const int32_t *trow = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
+    const int jmin = klo / BS, jmax = (khi - 1) / BS;
+    bool bad = false;
+    uint4 sk[2], sv[2];
+    auto fetch = [&](int t) {
+      const int kbase = (kt0 + t) * kKeys;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int kp = kbase + rr + 16 * half;
+        const int j = min(max(kp / BS, jmin), jmax);
+        int e = load_const(trow, j);
+        if (static_cast<uint32_t>(e) >= static_cast<uint32_t>(a.num_blocks)) {
+          bad = true;
+          e = 0;
+        }
+        const int64_t off = static_cast<int64_t>(e) * blk_bytes + (kp % BS) * (kHd * 2) + ch * 16;
+        sk[half] = *reinterpret_cast<const uint4 *>(kpool + off);
+        sv[half] = *reinterpret_cast<const uint4 *>(vpool + off);
+      }
+    };
+    auto stage = [&](int buf) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        *reinterpret_cast<uint4 *>(&s_k[buf][(rr + 16 * half) * kRowBytes + ch * 16]) = sk[half];
+        *reinterpret_cast<uint4 *>(&s_v[buf][(rr + 16 * half) * kRowBytes + ch * 16]) = sv[half];
+      }
+    };
+
+    float m_run[kCg], l_run[kCg];
+    f32x4_t acc[kCg][8];
+#pragma unroll
+    for (int cg = 0; cg < kCg; ++cg) {
+      m_run[cg] = -INFINITY;
+      l_run[cg] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[cg][e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    // one 16-key half of the staged tile in `buf`, keys kh0 .. kh0 + 15
+    auto half_tile = [&](int buf, int hh, int kh0, bool masked) {
+      V8 ka[4];
+      const uint8_t *krow = &s_k[buf][(hh * 16 + r16) * kRowBytes];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ka[j] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4 *>(krow + dbase(j, g4) * 2));
+      uint32_t x[4][4];
+      const uint8_t *vrow = &s_v[buf][(hh * 16 + 4 * g4) * kRowBytes + r16 * 16];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint4 w = *reinterpret_cast<const uint4 *>(vrow + c * kRowBytes);
+        // rows outside [klo, khi) hold bytes of no position (their p is 0,
+        // but NaN or Inf there would survive the product): zeroed
+        if (masked) {
+          const int kp = kh0 + 4 * g4 + c;
+          if (kp < klo || kp >= khi) w = make_uint4(0u, 0u, 0u, 0u);
+        }
+        x[c][0] = w.x;
+        x[c][1] = w.y;
+        x[c][2] = w.z;
+        x[c][3] = w.w;
+      }
+      V4 va[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        va[2 * k] = __builtin_bit_cast(V4, make_uint2(__builtin_amdgcn_perm(x[1][k], x[0][k], 0x05040100u),
+                                                      __builtin_amdgcn_perm(x[3][k], x[2][k], 0x05040100u)));
+        va[2 * k + 1] = __builtin_bit_cast(V4, make_uint2(__builtin_amdgcn_perm(x[1][k], x[0][k], 0x07060302u),
+                                                          __builtin_amdgcn_perm(x[3][k], x[2][k], 0x07060302u)));
+      }
+#pragma unroll
+      for (int cg = 0; cg < kCg; ++cg) {
+        f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sc = M::run(ka[j], qop[cg][j], sc);
+        float z[4];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          z[r4] = sc[r4] * a.scale_log2;
+          if (masked) {
+            const int kp = kh0 + 4 * g4 + r4;
+            z[r4] = (kp <= qp[cg] && kp >= lo_col[cg]) ? z[r4] : -INFINITY;
+          }
+        }
+        float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+        mx = xor32_max(xor16_max(mx));
+        const float m_new = fmaxf(m_run[cg], mx);
+        // a column that has seen no key yet keeps m = -inf: exponents are
+        // then taken against 0 so they give 0, not NaN
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run[cg] - m_use);
+        float p[4];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) p[r4] = __builtin_amdgcn_exp2f(z[r4] - m_use);
+        l_run[cg] = fmaf(l_run[cg], alpha, (p[0] + p[1]) + (p[2] + p[3]));
+        m_run[cg] = m_new;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[cg][e] *= alpha;
+        }
+        const V4 pb = __builtin_bit_cast(V4, make_uint2(M::pack2(p[0], p[1]), M::pack2(p[2], p[3])));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[cg][e] = M::run16(va[e], pb, acc[cg][e]);
+      }
+    };
+
+    fetch(0);
+    stage(0);
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      const int buf = t & 1;
+      if (t + 1 < ntiles) fetch(t + 1);             // in flight during this tile's compute
+      const int kbase = (kt0 + t) * kKeys;
+      if (!idle) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int kh0 = kbase + 16 * hh;
+          // halves past every column of the wave, or before every window
+          if (kh0 > wq1 || kh0 + 15 < wlo0) continue;
+          const bool masked = kh0 + 15 > wq0 || kh0 < wlo1 || kh0 < klo || kh0 + 15 >= khi;
+          if (masked)
+            half_tile(buf, hh, kh0, true);
+          else
+            half_tile(buf, hh, kh0, false);
+        }
+      }
+      if (t + 1 < ntiles) stage(buf ^ 1);
+      __syncthreads();
+    }
+
+    const float nanv = __builtin_nanf("");
+#pragma unroll
+    for (int cg = 0; cg < kCg; ++cg) {
+      const float l = xor32_sum(xor16_sum(l_run[cg]));
+      if (!valid[cg]) continue;
+      const float mul = bad ? nanv : 1.0f / l;
+      const int64_t idx = out_idx(cg);
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        store4(a.out, idx + 8 * r4, make_float4(acc[cg][0][r4], acc[cg][1][r4], acc[cg][2][r4], acc[cg][3][r4]), mul);
+        store4(a.out, idx + 8 * r4 + 4, make_float4(acc[cg][4][r4], acc[cg][5][r4], acc[cg][6][r4], acc[cg][7][r4]),
+               mul);
+      }
+    }
+  }
+};
+
+template <typename QS, int G, int BS>
+__global__ __launch_bounds__(kWaves * 64) void prefill_kernel(DecodeArgs a) {
+  Prefill<QS, G, BS>::run(a);
+}
+
+template <typename QS, int G, int BS>
+hipError_t launch_g(const DecodeArgs &a, hipStream_t s) {
+  constexpr int qb = Prefill<QS, G, BS>::kQb;
+  // an upper bound on the batch's (KV head, query block) items; the surplus
+  // workgroups find no block and exit
+  const int64_t items = static_cast<int64_t>(a.num_kv_heads) * ((a.num_tokens + qb - 1) / qb + a.num_seqs);
+  if (items > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_kernel<QS, G, BS>), dim3(static_cast<unsigned>(items)), dim3(kWaves * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename QS, int BS>
+hipError_t launch_bs(const DecodeArgs &a, hipStream_t s) {
+  switch (a.group) {
+    case 1: return launch_g<QS, 1, BS>(a, s);
+    case 2: return launch_g<QS, 2, BS>(a, s);
+    case 4: return launch_g<QS, 4, BS>(a, s);
+    case 8: return launch_g<QS, 8, BS>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename QS>
+hipError_t launch_q(const DecodeArgs &a, hipStream_t s) {
+  return a.block_size == 16 ? launch_bs<QS, 16>(a, s) : launch_bs<QS, 32>(a, s);
+}
+
+}  // namespace
+
+bool prefill_fast_applies(int q_dtype, int kv_dtype, const DecodeArgs &a) {
+  if (a.head_dim != kHd || (a.block_size != 16 && a.block_size != 32)) return false;
+  if ((q_dtype != kBF16 && q_dtype != kF16) || kv_dtype != q_dtype) return false;
+  return a.group == 1 || a.group == 2 || a.group == 4 || a.group == 8;
+}
+
+hipError_t launch_prefill_fast(int q_dtype, const DecodeArgs &a, hipStream_t s) {
+  return q_dtype == kBF16 ? launch_q<BF16S>(a, s) : launch_q<F16S>(a, s);
+}
+
+}  // namespace pa_impl

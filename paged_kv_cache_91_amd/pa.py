@@ -32,7 +32,7 @@ _ELEM = {PA_F32: 4, PA_F16: 2, PA_BF16: 2, PA_FP8_E4M3: 1}
 EXPORTED = ("pa_write_kv", "pa_decode", "pa_decode_workspace_bytes", "pa_copy_blocks",
             "pa_status_string", "pa_last_error", "pa_version", "pa_time_next_decode",
             "pa_decode_status", "pa_set_wait_polls", "pa_decode_noalloc", "pa_swap_blocks",
-            "pa_decode_window")
+            "pa_decode_window", "pa_prefill")
 PA_NOALLOC_SCRATCH_BYTES = 32 << 20
 PA_WS_CLEAN, PA_WS_MISPLACED, PA_WS_TIMED_OUT = 0, 1, 2
 
@@ -100,6 +100,8 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_window.argtypes = [vp, i32, i32, i32, pool_p, vp, i32, vp, i32, ctypes.c_float, vp, i32,
                                        vp, ctypes.c_size_t, vp]
         L.pa_decode_window.restype = ctypes.c_int
+        L.pa_prefill.argtypes = [vp, i32, i32, i32, pool_p, i32, vp, i32, vp, vp, i32, ctypes.c_float, vp, vp]
+        L.pa_prefill.restype = ctypes.c_int
         L.pa_swap_blocks.argtypes = [pool_p, pool_p, vp, i32, vp]
         L.pa_swap_blocks.restype = ctypes.c_int
         _lib = L
@@ -251,9 +253,34 @@ def pa_decode(q: torch.Tensor, pool: KvPool, block_tables: torch.Tensor,
                                       _ptr(block_tables, "block_tables"), maxb, _ptr(context_lens, "context_lens"),
                                       _window, float(scale), _ptr(out, "out"), int(partition_size), ws_ptr,
                                       ws_bytes, _stream(stream)),
-               "pa_decode_window")
+               "pa_decode_window", "pa_prefill")
     if own_ws is not None:
         workspace.record_stream(own_ws)
+    return out
+
+
+def pa_prefill(q: torch.Tensor, pool: KvPool, block_tables: torch.Tensor, context_lens: torch.Tensor,
+               query_start: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
+               window: int = 0, q_dtype: Optional[str] = None, stream=None) -> torch.Tensor:
+    """Causal prefill: ``q`` ``[T, Hq, D]`` packed rows, ``query_start`` int32
+    ``[S + 1]``; returns ``out`` ``[T, Hq, D]``."""
+    if q.dim() != 3:
+        raise ValueError("q must be [num_tokens, num_q_heads, head_dim]")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or query_start.dtype != torch.int32:
+        raise ValueError("block_tables, context_lens and query_start must be int32")
+    s = int(context_lens.shape[0])
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or query_start.shape != (s + 1,):
+        raise ValueError("block_tables must be [S, max_blocks], query_start [S + 1]")
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    t, hq, _ = q.shape
+    _check(lib().pa_prefill(_ptr(q, "q"), dtype_code(q, q_dtype), t, hq, ctypes.byref(pool), s,
+                            _ptr(block_tables, "block_tables"), int(block_tables.shape[1]),
+                            _ptr(context_lens, "context_lens"), _ptr(query_start, "query_start"), int(window),
+                            float(scale), _ptr(out, "out"), _stream(stream)),
+           "pa_prefill")
     return out
 
 
