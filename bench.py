@@ -67,7 +67,8 @@ def parse():
                     help="with --workload other than llama3-8b: comma-separated partition sizes to time "
                          "(default: -1, 0 and the batch's own or 256)")
     ap.add_argument("--workload", default="llama3-8b",
-                    choices=["llama3-8b", "mha-13b", "prefix-cow", "fp8-long", "window", "swap"],
+                    choices=["llama3-8b", "mha-13b", "prefix-cow", "fp8-long", "window", "swap", "prefill",
+                             "prefill-chunk"],
                     help="llama3-8b: the step above (default).  The others time pa_decode alone on the "
                          "13B-shaped fp16 batch, the prefix-sharing batch or the long-context fp8 batch "
                          "(one JSON line per partition setting)")
@@ -130,6 +131,8 @@ def main():
         return calibrate_copy(args.calibrate_copy, pa, torch, dev)
     if args.workload == "swap":
         return swap_workload(args, pa, torch, dev)
+    if args.workload.startswith("prefill"):
+        return prefill_workload(args, pa, W, torch, dev)
     if args.workload != "llama3-8b":
         return other_workload(args, pa, W, torch, dev)
 
@@ -429,6 +432,67 @@ def window_batch(W):
     return W.build_decode(9, name="window-4096-bf16", q_dtype="bf16", kv_dtype="bf16", num_q_heads=32,
                           num_kv_heads=8, head_dim=128, block_size=16, num_blocks=need + 64,
                           context_lens=lens, rng=rng)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
+
+
+def prefill_workload(args, pa, W, torch, dev):
+    """pa_prefill on the 8B layer shape (bf16, 32 q heads on 8 KV heads, head
+    dim 128, block 16).  "prefill": 16 whole prompts of 2048 positions;
+    "prefill-chunk": 16 chunks of 512 queries after cached prefixes uniform
+    in [0, 3584].  Work = the attended (query, key) pairs x query heads x 4 x
+    head_dim flops (q.K^T and P.V, 2 each), against the dense bf16 peak."""
+    import numpy as np
+    rng = np.random.default_rng(13)
+    S = 16
+    if args.workload == "prefill":
+        lens = np.full(S, 2048)
+        qlens = lens.copy()
+    else:
+        qlens = np.full(S, 512)
+        lens = rng.integers(0, 3585, size=S) + qlens
+    need = int(sum(-(-int(n) // 16) for n in lens))
+    wl = W.build_decode(13, name=args.workload, q_dtype="bf16", kv_dtype="bf16", num_q_heads=32, num_kv_heads=8,
+                        head_dim=128, block_size=16, num_blocks=need + 16, context_lens=lens, rng=rng)
+    T = int(qlens.sum())
+    q_host = W.cast_f32(W.normal_f32(13, 9, T * 32 * 128), "bf16").reshape(T, 32, 128)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    kp, vp, q = bf16(wl.k_pool), bf16(wl.v_pool), bf16(q_host)
+    pool = pa.make_pool(kp, vp)
+    tb = torch.from_numpy(wl.block_tables.astype(np.int32)).to(dev)
+    ctx = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    qs = torch.from_numpy(np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)).to(dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    pairs = sum(int(sum(range(n - L + 1, n + 1))) for n, L in zip(lens, qlens))
+    flops = pairs * 32 * 4 * 128
+    for _ in range(max(args.warmup, 3)):
+        pa.pa_prefill(q, pool, tb, ctx, qs, wl.scale, out=out, stream=stream)
+    steps = max(3, min(args.steps, 30))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        pa.pa_prefill(q, pool, tb, ctx, qs, wl.scale, out=out, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    med = us[len(us) // 2]
+    tflops = flops / (med * 1e-6) / 1e12
+    assert bool(torch.isfinite(out.float()).all()), "non-finite output"
+    print(json.dumps({
+        "workload": args.workload, "num_seqs": S, "query_rows": T, "context_tokens": int(lens.sum()),
+        "attended_pairs": pairs, "flops": flops,
+        "prefill_us": {"median": round(med, 1), "p10": round(us[len(us) // 10], 1),
+                       "p90": round(us[(9 * len(us)) // 10], 1), "calls": steps},
+        "tflops": round(tflops, 1), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+        "frac_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "tokens_per_s_per_layer": round(T / (med * 1e-6), 1),
+    }), flush=True)
 
 
 def swap_workload(args, pa, torch, dev):

@@ -215,3 +215,88 @@ def test_swap_refuses_pageable_host_memory():
     torch.cuda.synchronize()
     assert not pageable.any()
     assert bool((ks == 1).all())
+
+
+# ---------------------------------------------------------------------------
+# prefix cache -> chunked prefill -> decode
+# ---------------------------------------------------------------------------
+
+def _kv_rows(toks, positions, hkv, d, salt):
+    """K (salt 0) or V (salt 1) rows of positions given their tokens: a fixed
+    function of (token, position), so a cached prefix holds exactly the rows
+    a fresh computation would write."""
+    out = np.empty((len(positions), hkv, d), np.float32)
+    for i, (t, p) in enumerate(zip(toks, positions)):
+        out[i] = np.random.default_rng([int(t), int(p), salt]).standard_normal((hkv, d), dtype=np.float32)
+    return W.cast_f32(out, "bf16")
+
+
+def test_prefix_cache_feeds_prefill_and_decode():
+    from paged_kv_cache_91_amd.prefix_cache import PrefixCachingAllocator
+    bs, hq, hkv, d, nblocks = 16, 32, 8, 128, 96
+    rng = np.random.default_rng(700)
+    sys_prompt = list(rng.integers(0, 32000, size=80))
+    prompt_a = sys_prompt + list(rng.integers(0, 32000, size=37))
+    prompt_b = sys_prompt + list(rng.integers(0, 32000, size=50))
+    alloc = PrefixCachingAllocator(nblocks, bs, free_order=rng.permutation(nblocks))
+    kd = torch.full((nblocks, hkv, bs, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    vd = torch.full_like(kd, float("nan"))
+    pool = pa.make_pool(kd, vd)
+
+    def write(seq, toks, start):
+        pos = np.arange(start, len(toks))
+        slots = torch.from_numpy(alloc.slots(seq, start, len(toks))).to(DEV)
+        pa.pa_write_kv(to_dev(_kv_rows(toks[start:], pos, hkv, d, 0), "bf16"),
+                       to_dev(_kv_rows(toks[start:], pos, hkv, d, 1), "bf16"), slots, pool)
+
+    _, cached_a = alloc.add_prompt(0, prompt_a)
+    assert cached_a == 0
+    write(0, prompt_a, 0)
+    alloc.commit(0, prompt_a)
+    table_b, cached_b = alloc.add_prompt(1, prompt_b)
+    assert cached_b == 80 and table_b[:5] == alloc.block_table(0)[:5]
+    torch.cuda.synchronize()
+    shared_before = kd[torch.tensor(table_b[:5], device=DEV)].clone()
+    write(1, prompt_b, cached_b)                 # only B's own positions
+    # chunked prefill of B's 50 new positions
+    n_b, L = len(prompt_b), len(prompt_b) - cached_b
+    q = W.cast_f32(rng.standard_normal((L, hq, d)).astype(np.float32), "bf16")
+    maxb = 12
+    tables = np.zeros((1, maxb), np.int32)
+    tables[0, :len(table_b)] = table_b
+    got = out_f64(pa.pa_prefill(to_dev(q, "bf16"), pool, torch.from_numpy(tables).to(DEV),
+                                torch.tensor([n_b], dtype=torch.int32, device=DEV),
+                                torch.tensor([0, L], dtype=torch.int32, device=DEV), 1 / np.sqrt(d)))
+    # the oracle on B's rows laid out without any sharing
+    nb = -(-n_b // bs)
+    kp = np.zeros((nb, hkv, bs, d), np.uint16)
+    vp = np.zeros_like(kp)
+    kp, vp = oracle.oracle_write(_kv_rows(prompt_b, range(n_b), hkv, d, 0), _kv_rows(prompt_b, range(n_b), hkv, d, 1),
+                                 "bf16", np.arange(n_b), kp, vp, "bf16")
+    own = np.arange(nb, dtype=np.int32)[None]
+    scale = float(np.float32(1 / np.sqrt(d)))
+    ref = oracle.oracle_prefill(q, "bf16", kp, vp, "bf16", own, np.array([n_b]), np.array([0, L]), scale)
+    assert max_err(got, ref) <= 2e-2
+    # one decode step of B: its next token goes to a fresh slot, then decode
+    slots, pairs = alloc.append_tokens(1, 1)
+    assert not pairs
+    nxt = list(rng.integers(0, 32000, size=1))
+    pa.pa_write_kv(to_dev(_kv_rows(nxt, [n_b], hkv, d, 0), "bf16"), to_dev(_kv_rows(nxt, [n_b], hkv, d, 1), "bf16"),
+                   torch.from_numpy(slots).to(DEV), pool)
+    tables[0, :len(alloc.block_table(1))] = alloc.block_table(1)
+    qd = W.cast_f32(rng.standard_normal((1, hq, d)).astype(np.float32), "bf16")
+    dec = out_f64(pa.pa_decode(to_dev(qd, "bf16"), pool, torch.from_numpy(tables).to(DEV),
+                               torch.tensor([n_b + 1], dtype=torch.int32, device=DEV), scale,
+                               partition_size=pa.PA_PARTITION_AUTO))
+    full = prompt_b + nxt
+    nb2 = -(-(n_b + 1) // bs)
+    kp2, vp2 = oracle.oracle_write(_kv_rows(full, range(n_b + 1), hkv, d, 0), _kv_rows(full, range(n_b + 1), hkv, d, 1),
+                                   "bf16", np.arange(n_b + 1), np.zeros((nb2, hkv, bs, d), np.uint16),
+                                   np.zeros((nb2, hkv, bs, d), np.uint16), "bf16")
+    ref_dec = oracle.oracle_decode(qd, "bf16", kp2, vp2, "bf16", np.arange(nb2, dtype=np.int32)[None],
+                                   np.array([n_b + 1]), scale)
+    assert max_err(dec, ref_dec) <= 2e-2
+    # the shared prefix blocks were never written by B
+    torch.cuda.synchronize()
+    assert torch.equal(kd[torch.tensor(table_b[:5], device=DEV)].view(torch.int16), shared_before.view(torch.int16))
+    alloc.check()
