@@ -185,7 +185,9 @@ __device__ __forceinline__ int load_const(const int32_t *p, int64_t i) {
 // NW waves share one partition: wave w takes tiles w, w+NW, w+2NW, ...; the
 // waves' softmax states are merged through LDS, so a partition costs one
 // partial write however many waves stream it.
-template <typename QS, typename KS, int GT, int BS, int NW>
+// WIN: the balanced split with a sliding window (per-sequence first tile);
+// without it the window fields fold to zero.
+template <typename QS, typename KS, int GT, int BS, int NW, bool WIN = false>
 struct Fast {
   using M = Mma<QS>;
   using V8 = typename M::V8;
@@ -475,13 +477,19 @@ struct Fast {
     int64_t G;
   };
   static __device__ __forceinline__ int tiles_of(int n, int maxn, int window) {
+    if constexpr (!WIN) return (n > 0 && n <= maxn) ? (n + kTile - 1) / kTile : 0;
     return (n > 0 && n <= maxn) ? (n + kTile - 1) / kTile - window_lo(n, window) / kTile : 0;
   }
   static __device__ __forceinline__ void set_seq(Cursor &c, int n, int maxn, int window) {
     c.n = n;
     c.nts = tiles_of(n, maxn, window);
-    c.lo = (n > 0 && n <= maxn) ? window_lo(n, window) : 0;
-    c.t0 = c.lo / kTile;
+    if constexpr (WIN) {
+      c.lo = (n > 0 && n <= maxn) ? window_lo(n, window) : 0;
+      c.t0 = c.lo / kTile;
+    } else {
+      c.lo = 0;
+      c.t0 = 0;
+    }
   }
   // next tile in list order (past the last one the cursor parks on s = S);
   // n_lane holds the first 64 sequences' lengths, one per lane
@@ -1577,7 +1585,7 @@ __global__ __launch_bounds__(64) void merge_parts_kernel(DecodeArgs a) {
 // workgroups of the fixed-partition split per compute unit (one wave each)
 constexpr int kSplitWgsPerCu = 32;
 
-template <typename QS, typename KS, int GT, int BS>
+template <typename QS, typename KS, int GT, int BS, bool WIN>
 // The fields the launch's first loads depend on come as separate scalar
 // arguments ahead of the struct, so that they can arrive preloaded in SGPRs
 // (kernel-argument preloading) instead of through a load of the argument
@@ -1592,7 +1600,7 @@ __global__ __launch_bounds__(512) void decode_pair_kernel(const int32_t *ctx, in
   a.num_kv_heads = num_kv_heads;
   a.head_groups = head_groups;
   a.num_xcd = num_xcd;
-  Fast<QS, KS, GT, BS, 1>::run_pair(a);
+  Fast<QS, KS, GT, BS, 1, WIN>::run_pair(a);
 }
 
 // Grid of the balanced split: one 8-wave workgroup (4 streaming waves, one
@@ -1600,11 +1608,11 @@ __global__ __launch_bounds__(512) void decode_pair_kernel(const int32_t *ctx, in
 // kernel does not touch brings a workgroup's LDS above half of the 160 KiB a
 // compute unit has, which keeps a second workgroup off the same unit.
 constexpr int kPairLdsBytes = 84 * 1024;
-template <typename QS, typename KS, int GT, int BS>
-hipError_t launch_stream_gt(const DecodeArgs &a, hipStream_t s, const LaunchEvents &ev) {
+template <typename QS, typename KS, int GT, int BS, bool WIN>
+hipError_t launch_stream_win(const DecodeArgs &a, hipStream_t s, const LaunchEvents &ev) {
   static const int fixed = [] {
     hipFuncAttributes at{};
-    if (hipFuncGetAttributes(&at, reinterpret_cast<const void *>(&decode_pair_kernel<QS, KS, GT, BS>)) !=
+    if (hipFuncGetAttributes(&at, reinterpret_cast<const void *>(&decode_pair_kernel<QS, KS, GT, BS, WIN>)) !=
         hipSuccess)
       return 0;
     return static_cast<int>(at.sharedSizeBytes);
@@ -1615,9 +1623,15 @@ hipError_t launch_stream_gt(const DecodeArgs &a, hipStream_t s, const LaunchEven
   // range codes (4 bytes per range), at least up to kPairLdsBytes in all
   const int table = (4 * wgs + 1) * 8 + 4 * wgs * 4;
   const int dyn = max(table, kPairLdsBytes - fixed);
-  hipExtLaunchKernelGGL((decode_pair_kernel<QS, KS, GT, BS>), dim3(wgs), dim3(512), dyn, s, ev.start, ev.stop, 0,
-                        a.ctx, a.ctl, a.num_seqs, a.max_blocks, a.num_kv_heads, a.head_groups, a.num_xcd, a);
+  hipExtLaunchKernelGGL((decode_pair_kernel<QS, KS, GT, BS, WIN>), dim3(wgs), dim3(512), dyn, s, ev.start, ev.stop,
+                        0, a.ctx, a.ctl, a.num_seqs, a.max_blocks, a.num_kv_heads, a.head_groups, a.num_xcd, a);
   return hipGetLastError();
+}
+
+template <typename QS, typename KS, int GT, int BS>
+hipError_t launch_stream_gt(const DecodeArgs &a, hipStream_t s, const LaunchEvents &ev) {
+  return a.window > 0 ? launch_stream_win<QS, KS, GT, BS, true>(a, s, ev)
+                      : launch_stream_win<QS, KS, GT, BS, false>(a, s, ev);
 }
 
 template <typename QS, typename KS, int BS>

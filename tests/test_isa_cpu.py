@@ -22,7 +22,7 @@ import pytest
 
 from paged_kv_cache_91_amd import build as B
 
-KERNEL = "_ZN7pa_impl12_GLOBAL__N_118decode_pair_kernelINS0_5BF16SES2_Li4ELi16EEEvPKiPiiiiiiNS_10DecodeArgsE"
+KERNEL = "_ZN7pa_impl12_GLOBAL__N_118decode_pair_kernelINS0_5BF16SES2_Li4ELi16ELb0EEEvPKiPiiiiiiNS_10DecodeArgsE"
 
 
 @pytest.fixture(scope="module")
