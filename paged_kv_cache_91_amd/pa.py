@@ -253,7 +253,7 @@ def pa_decode(q: torch.Tensor, pool: KvPool, block_tables: torch.Tensor,
                                       _ptr(block_tables, "block_tables"), maxb, _ptr(context_lens, "context_lens"),
                                       _window, float(scale), _ptr(out, "out"), int(partition_size), ws_ptr,
                                       ws_bytes, _stream(stream)),
-               "pa_decode_window", "pa_prefill")
+               "pa_decode_window")
     if own_ws is not None:
         workspace.record_stream(own_ws)
     return out
