@@ -18,15 +18,16 @@
 // four waves (padded rows; double-buffered, the next tile's global loads in
 // flight during the current tile's compute).
 //
-// Per 16-key half of a tile and column group (the decode kernel's layout with
-// query columns in place of heads):
-//   S^T = K . Q^T   four v_mfma_f32_16x16x32 (A = 16 key rows from LDS,
-//                   B = the column group's q), lane l holds keys 4*(l/16)+r
-//                   of column l%16;
-//   online softmax per column in the base-2 domain, causal (and window) mask
-//   only on tiles that reach past a column's position;
-//   O^T += V^T . P  eight v_mfma_f32_16x16x16 (A = V rows from LDS repacked
-//                   with v_perm, B = the probabilities in place).
+// Per 32-key tile and column group (the decode kernel's layout with query
+// columns in place of heads):
+//   S^T = K . Q^T   per 16-key half, four v_mfma_f32_16x16x32 (A = 16 key
+//                   rows from LDS, B = the column group's q); lane l holds
+//                   keys 4*(l/16)+r of each half for column l%16;
+//   online softmax per column in the base-2 domain over the 32 keys, causal
+//   (and window) mask only on tiles that reach past a column's position;
+//   O^T += V^T . P  eight v_mfma_f32_16x16x32 over all 32 keys (A = V rows
+//                   from LDS repacked with v_perm into the probabilities'
+//                   key order, B = the probabilities in place).
 // Blocks are ordered so that all blocks of one (sequence, KV head) land on
 // one XCD (their K/V is re-read from that XCD's L2), last block first.
 
@@ -189,29 +190,44 @@ struct Prefill {
     const int32_t *trow = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
     const int jmin = klo / BS, jmax = (khi - 1) / BS;
     bool bad = false;
-    uint4 sk[2], sv[2];
-    auto fetch = [&](int t) {
-      const int kbase = (kt0 + t) * kKeys;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int kp = kbase + rr + 16 * half;
-        const int j = min(max(kp / BS, jmin), jmax);
-        int e = load_const(trow, j);
-        if (static_cast<uint32_t>(e) >= static_cast<uint32_t>(a.num_blocks)) {
-          bad = true;
-          e = 0;
-        }
-        const int64_t off = static_cast<int64_t>(e) * blk_bytes + (kp % BS) * (kHd * 2) + ch * 16;
-        sk[half] = *reinterpret_cast<const uint4 *>(kpool + off);
-        sv[half] = *reinterpret_cast<const uint4 *>(vpool + off);
+    // byte offset of the 16-byte chunk of row rr of the 16 positions from
+    // kb16 (a multiple of 16, so all 16 sit in one block: the table entry is
+    // uniform and read with a scalar load)
+    auto offset_of = [&](int kb16) {
+      const int j = uniform(min(max(kb16 / BS, jmin), jmax));
+      int e = load_const(trow, j);
+      if (static_cast<uint32_t>(e) >= static_cast<uint32_t>(a.num_blocks)) {
+        bad = true;
+        e = 0;
       }
+      return static_cast<int64_t>(e) * blk_bytes + (kb16 % BS + rr) * (kHd * 2) + ch * 16;
     };
-    auto stage = [&](int buf) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        *reinterpret_cast<uint4 *>(&s_k[buf][(rr + 16 * half) * kRowBytes + ch * 16]) = sk[half];
-        *reinterpret_cast<uint4 *>(&s_v[buf][(rr + 16 * half) * kRowBytes + ch * 16]) = sv[half];
-      }
+    // the next tile's chunks, held in named registers (an array here ends up
+    // in scratch memory, which would wait for the loads at once)
+    uint4 sk0, sk1, sv0, sv1;
+    auto fetch = [&](int t) {
+      const int kbase = uniform((kt0 + t) * kKeys);
+      const int64_t o0 = offset_of(kbase), o1 = offset_of(kbase + 16);
+      sk0 = *reinterpret_cast<const uint4 *>(kpool + o0);
+      sv0 = *reinterpret_cast<const uint4 *>(vpool + o0);
+      sk1 = *reinterpret_cast<const uint4 *>(kpool + o1);
+      sv1 = *reinterpret_cast<const uint4 *>(vpool + o1);
+    };
+    // V rows of positions outside [klo, khi) hold bytes of no position
+    // attended here: their probabilities are 0, but NaN or Inf would survive
+    // the product, so they are staged as zeros
+    auto stage = [&](int buf, int t) {
+      const int kbase = (kt0 + t) * kKeys;
+      // all-ones or all-zeros masks (a select of whole vectors becomes a
+      // scratch-memory lookup)
+      const uint32_t m0 = (kbase + rr >= klo && kbase + rr < khi) ? ~0u : 0u;
+      const uint32_t m1 = (kbase + rr + 16 >= klo && kbase + rr + 16 < khi) ? ~0u : 0u;
+      *reinterpret_cast<uint4 *>(&s_k[buf][rr * kRowBytes + ch * 16]) = sk0;
+      *reinterpret_cast<uint4 *>(&s_v[buf][rr * kRowBytes + ch * 16]) =
+          make_uint4(sv0.x & m0, sv0.y & m0, sv0.z & m0, sv0.w & m0);
+      *reinterpret_cast<uint4 *>(&s_k[buf][(rr + 16) * kRowBytes + ch * 16]) = sk1;
+      *reinterpret_cast<uint4 *>(&s_v[buf][(rr + 16) * kRowBytes + ch * 16]) =
+          make_uint4(sv1.x & m1, sv1.y & m1, sv1.z & m1, sv1.w & m1);
     };
 
     float m_run[kCg], l_run[kCg];
@@ -224,93 +240,106 @@ struct Prefill {
       for (int e = 0; e < 8; ++e) acc[cg][e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
-    // one 16-key half of the staged tile in `buf`, keys kh0 .. kh0 + 15
-    auto half_tile = [&](int buf, int hh, int kh0, bool masked) {
-      V8 ka[4];
-      const uint8_t *krow = &s_k[buf][(hh * 16 + r16) * kRowBytes];
+    // One staged 32-key tile (keys kbase .. kbase + 31) against the wave's
+    // columns.  q.K^T runs per 16-key half (A = 16 key rows); lane (r16, g4)
+    // then holds, for its column r16, the keys of slots j < 8: half j / 4,
+    // key 4 * g4 + j % 4 -- exactly the K-slot order of a 16x16x32 MFMA, so
+    // P.V is eight 16x16x32 MFMAs over all 32 keys (A = V restricted to dims
+    // 8i + e in the same slot order, B = the probabilities in place), and the
+    // online softmax updates once per tile.
+    auto tile = [&](int buf, int kbase, bool masked) {
+      float z[kCg][8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ka[j] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4 *>(krow + dbase(j, g4) * 2));
-      uint32_t x[4][4];
-      const uint8_t *vrow = &s_v[buf][(hh * 16 + 4 * g4) * kRowBytes + r16 * 16];
+      for (int hh = 0; hh < 2; ++hh) {
+        V8 ka[4];
+        const uint8_t *krow = &s_k[buf][(hh * 16 + r16) * kRowBytes];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint4 w = *reinterpret_cast<const uint4 *>(vrow + c * kRowBytes);
-        // rows outside [klo, khi) hold bytes of no position (their p is 0,
-        // but NaN or Inf there would survive the product): zeroed
-        if (masked) {
-          const int kp = kh0 + 4 * g4 + c;
-          if (kp < klo || kp >= khi) w = make_uint4(0u, 0u, 0u, 0u);
+        for (int j = 0; j < 4; ++j) ka[j] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4 *>(krow + dbase(j, g4) * 2));
+#pragma unroll
+        for (int cg = 0; cg < kCg; ++cg) {
+          f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sc = M::run(ka[j], qop[cg][j], sc);
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) z[cg][4 * hh + r4] = sc[r4] * a.scale_log2;
         }
-        x[c][0] = w.x;
-        x[c][1] = w.y;
-        x[c][2] = w.z;
-        x[c][3] = w.w;
       }
-      V4 va[8];
+      // causal and window masks, on tiles that reach past a column's position
+      // or start before its window (one uniform branch)
+      if (masked) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        va[2 * k] = __builtin_bit_cast(V4, make_uint2(__builtin_amdgcn_perm(x[1][k], x[0][k], 0x05040100u),
-                                                      __builtin_amdgcn_perm(x[3][k], x[2][k], 0x05040100u)));
-        va[2 * k + 1] = __builtin_bit_cast(V4, make_uint2(__builtin_amdgcn_perm(x[1][k], x[0][k], 0x07060302u),
-                                                          __builtin_amdgcn_perm(x[3][k], x[2][k], 0x07060302u)));
-      }
+        for (int cg = 0; cg < kCg; ++cg) {
+          const int hi_off = qp[cg] - kbase - 4 * g4, lo_off = lo_col[cg] - kbase - 4 * g4;
 #pragma unroll
-      for (int cg = 0; cg < kCg; ++cg) {
-        f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sc = M::run(ka[j], qop[cg][j], sc);
-        float z[4];
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          z[r4] = sc[r4] * a.scale_log2;
-          if (masked) {
-            const int kp = kh0 + 4 * g4 + r4;
-            z[r4] = (kp <= qp[cg] && kp >= lo_col[cg]) ? z[r4] : -INFINITY;
+          for (int j = 0; j < 8; ++j) {
+            const int off = 16 * (j >> 2) + (j & 3);
+            z[cg][j] = (off <= hi_off && off >= lo_off) ? z[cg][j] : -INFINITY;
           }
         }
-        float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      }
+      V8 pb[kCg];
+#pragma unroll
+      for (int cg = 0; cg < kCg; ++cg) {
+        float mx = z[cg][0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, z[cg][j]);
         mx = xor32_max(xor16_max(mx));
         const float m_new = fmaxf(m_run[cg], mx);
         // a column that has seen no key yet keeps m = -inf: exponents are
         // then taken against 0 so they give 0, not NaN
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m_run[cg] - m_use);
-        float p[4];
+        float p[8], ps = 0.0f;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) p[r4] = __builtin_amdgcn_exp2f(z[r4] - m_use);
-        l_run[cg] = fmaf(l_run[cg], alpha, (p[0] + p[1]) + (p[2] + p[3]));
+        for (int j = 0; j < 8; ++j) {
+          p[j] = __builtin_amdgcn_exp2f(z[cg][j] - m_use);
+          ps += p[j];
+        }
+        l_run[cg] = fmaf(l_run[cg], alpha, ps);
         m_run[cg] = m_new;
         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[cg][e] *= alpha;
         }
-        const V4 pb = __builtin_bit_cast(V4, make_uint2(M::pack2(p[0], p[1]), M::pack2(p[2], p[3])));
+        pb[cg] = __builtin_bit_cast(V8, make_uint4(M::pack2(p[0], p[1]), M::pack2(p[2], p[3]), M::pack2(p[4], p[5]),
+                                                   M::pack2(p[6], p[7])));
+      }
+      // A of MFMA e: element e (dims 8 * r16 + e) of the V rows of the
+      // lane's 8 key slots, two 16-bit values a dword, read per dword pair
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[cg][e] = M::run16(va[e], pb, acc[cg][e]);
+      for (int ep = 0; ep < 4; ++ep) {
+        uint32_t x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int row = 16 * (j >> 2) + 4 * g4 + (j & 3);
+          x[j] = *reinterpret_cast<const uint32_t *>(&s_v[buf][row * kRowBytes + r16 * 16 + 4 * ep]);
+        }
+#pragma unroll
+        for (int eo = 0; eo < 2; ++eo) {
+          const uint32_t sel = eo ? 0x07060302u : 0x05040100u;
+          const V8 va = __builtin_bit_cast(V8, make_uint4(__builtin_amdgcn_perm(x[1], x[0], sel),
+                                                          __builtin_amdgcn_perm(x[3], x[2], sel),
+                                                          __builtin_amdgcn_perm(x[5], x[4], sel),
+                                                          __builtin_amdgcn_perm(x[7], x[6], sel)));
+#pragma unroll
+          for (int cg = 0; cg < kCg; ++cg) acc[cg][2 * ep + eo] = M::run(va, pb[cg], acc[cg][2 * ep + eo]);
+        }
       }
     };
 
     fetch(0);
-    stage(0);
+    stage(0, 0);
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
       const int buf = t & 1;
       if (t + 1 < ntiles) fetch(t + 1);             // in flight during this tile's compute
       const int kbase = (kt0 + t) * kKeys;
-      if (!idle) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int kh0 = kbase + 16 * hh;
-          // halves past every column of the wave, or before every window
-          if (kh0 > wq1 || kh0 + 15 < wlo0) continue;
-          const bool masked = kh0 + 15 > wq0 || kh0 < wlo1 || kh0 < klo || kh0 + 15 >= khi;
-          if (masked)
-            half_tile(buf, hh, kh0, true);
-          else
-            half_tile(buf, hh, kh0, false);
-        }
+      // tiles past every column of the wave, or before every window, are skipped
+      if (!idle && kbase <= wq1 && kbase + kKeys - 1 >= wlo0) {
+        const bool masked = kbase + kKeys - 1 > wq0 || kbase < wlo1 || kbase < klo || kbase + kKeys - 1 >= khi;
+        tile(buf, kbase, masked);
       }
-      if (t + 1 < ntiles) stage(buf ^ 1);
+      if (t + 1 < ntiles) stage(buf ^ 1, t + 1);
       __syncthreads();
     }
 
