@@ -47,6 +47,27 @@ constexpr int kKeys = 32;                  // keys per staged tile
 constexpr int kRowBytes = kHd * 2 + 16;    // LDS row stride: 16 lanes reading one column of 16 rows spread over the banks
 constexpr int kWaves = 4;
 constexpr int kCg = 2;                     // column groups (16 columns each) per wave
+constexpr float kLazy = 8.0f;              // base-2 headroom before the running max moves
+
+// IEEE maximum (NaN-propagating): v_maximum3_f32 on gfx950, with none of the
+// quieting moves that fmaxf's operands get
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max3(float a, float b, float c) { return max2(max2(a, b), c); }
+__device__ __forceinline__ float lanes16_max(float x) {        // over lanes l, l ^ 16, l ^ 32, l ^ 48
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap16(a, b);
+  x = max2(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  a = b = __builtin_bit_cast(uint32_t, x);
+  swap32(a, b);
+  return max2(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+
+typedef short tr16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 read_tr(const uint8_t *lds) {
+  const tr16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) tr16x4_t *)(reinterpret_cast<uintptr_t>(lds)));
+  return __builtin_bit_cast(uint2, v);
+}
 
 typedef const __attribute__((address_space(4))) int32_t cint32_t;
 __device__ __forceinline__ int load_const(const int32_t *p, int64_t i) { return ((cint32_t *)p)[i]; }
@@ -136,8 +157,8 @@ struct Prefill {
       qp[cg] = pb0 + (wave * kCg + cg) * kPos + r16 / G;
       valid[cg] = qp[cg] < pb1;
     }
-    auto out_idx = [&](int cg) {
-      return (static_cast<int64_t>(q0 + qp[cg] - P0) * a.num_q_heads + h) * kHd + 32 * g4;
+    auto out_idx = [&](int cg) {           // the column's output row
+      return (static_cast<int64_t>(q0 + qp[cg] - P0) * a.num_q_heads + h) * kHd;
     };
     if (bad_len) {
       const float nanv = __builtin_nanf("");
@@ -145,11 +166,14 @@ struct Prefill {
       for (int cg = 0; cg < kCg; ++cg)
         if (valid[cg] && qp[cg] >= pb0)
 #pragma unroll
-          for (int r4 = 0; r4 < 8; ++r4) store4(a.out, out_idx(cg) + 4 * r4, make_float4(nanv, nanv, nanv, nanv), 1.0f);
+          for (int r4 = 0; r4 < 8; ++r4)
+            store4(a.out, out_idx(cg) + 32 * g4 + 4 * r4, make_float4(nanv, nanv, nanv, nanv), 1.0f);
       return;
     }
 
     // q of each column as the MFMA B operand (zero for columns past the block)
+    const uint32_t qsign = a.scale_log2 < 0.0f ? 0x80008000u : 0u;
+    const float sl = fabsf(a.scale_log2);
     V8 qop[kCg][4];
 #pragma unroll
     for (int cg = 0; cg < kCg; ++cg) {
@@ -159,6 +183,12 @@ struct Prefill {
       for (int j = 0; j < 4; ++j) {
         uint4 w = make_uint4(0u, 0u, 0u, 0u);
         if (valid[cg]) w = *reinterpret_cast<const uint4 *>(qrow + dbase(j, g4));
+        // a negative scale moves to q (a sign flip, exact), so that the
+        // score scale sl below is >= 0 and max(sl * s) = sl * max(s)
+        w.x ^= qsign;
+        w.y ^= qsign;
+        w.z ^= qsign;
+        w.w ^= qsign;
         qop[cg][j] = __builtin_bit_cast(V8, w);
       }
     }
@@ -230,6 +260,14 @@ struct Prefill {
           make_uint4(sv1.x & m1, sv1.y & m1, sv1.z & m1, sv1.w & m1);
     };
 
+    // Transposing read (ds_read_b64_tr_b16): within each 16-lane block, lane
+    // 4i + k receives element k of the 4-element pieces named by lanes i,
+    // i + 4, i + 8 and i + 12.  Lane (r16, g4) names the piece of key
+    // 4 g4 + r16 / 4 (16 more for the upper read) at dims 4 (r16 % 4) .. + 3
+    // of the MFMA's 16, so lane (m, g4) receives dim m at keys 4 g4 .. + 3:
+    // the key slots of the probabilities in B.
+    const int vt_off = (4 * g4 + (r16 >> 2)) * kRowBytes + 8 * (r16 & 3);
+
     float m_run[kCg], l_run[kCg];
     f32x4_t acc[kCg][8];
 #pragma unroll
@@ -245,10 +283,16 @@ struct Prefill {
     // then holds, for its column r16, the keys of slots j < 8: half j / 4,
     // key 4 * g4 + j % 4 -- exactly the K-slot order of a 16x16x32 MFMA, so
     // P.V is eight 16x16x32 MFMAs over all 32 keys (A = V restricted to dims
-    // 8i + e in the same slot order, B = the probabilities in place), and the
-    // online softmax updates once per tile.
+    // 8i + e in the same slot order, B = the probabilities in place).
+    //
+    // Online softmax in the base-2 domain, updated once per tile.  The
+    // running max m of a column is only moved (and acc, l rescaled) when the
+    // tile's max exceeds it by more than kLazy: otherwise the exponents are
+    // taken against the old m, which gives the same softmax (it is invariant
+    // to the shift) with probabilities up to 2^kLazy, far inside the 16-bit
+    // operand's range and with the same relative rounding.
     auto tile = [&](int buf, int kbase, bool masked) {
-      float z[kCg][8];
+      float z[kCg][8];                 // raw dot products
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         V8 ka[4];
@@ -261,7 +305,7 @@ struct Prefill {
 #pragma unroll
           for (int j = 0; j < 4; ++j) sc = M::run(ka[j], qop[cg][j], sc);
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) z[cg][4 * hh + r4] = sc[r4] * a.scale_log2;
+          for (int r4 = 0; r4 < 4; ++r4) z[cg][4 * hh + r4] = sc[r4];
         }
       }
       // causal and window masks, on tiles that reach past a column's position
@@ -277,53 +321,54 @@ struct Prefill {
           }
         }
       }
-      V8 pb[kCg];
+      float mz[kCg];
+      bool need = false;
 #pragma unroll
       for (int cg = 0; cg < kCg; ++cg) {
-        float mx = z[cg][0];
+        const float mx = lanes16_max(max3(max3(z[cg][0], z[cg][1], z[cg][2]), max3(z[cg][3], z[cg][4], z[cg][5]),
+                                          max2(z[cg][6], z[cg][7])));
+        mz[cg] = mx == -INFINITY ? -INFINITY : mx * sl;           // sl = 0 must not give NaN
+        need |= mz[cg] > m_run[cg] + kLazy;                       // true on a column's first keys
+      }
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
-        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, z[cg][j]);
-        mx = xor32_max(xor16_max(mx));
-        const float m_new = fmaxf(m_run[cg], mx);
-        // a column that has seen no key yet keeps m = -inf: exponents are
-        // then taken against 0 so they give 0, not NaN
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run[cg] - m_use);
-        float p[8], ps = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(z[cg][j] - m_use);
-          ps += p[j];
-        }
-        l_run[cg] = fmaf(l_run[cg], alpha, ps);
-        m_run[cg] = m_new;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+        for (int cg = 0; cg < kCg; ++cg) {
+          const float m_new = max2(m_run[cg], mz[cg]);
+          // a column that has seen no key keeps m = -inf; alpha is then 0
+          const float alpha = __builtin_amdgcn_exp2f(m_run[cg] - (m_new == -INFINITY ? 0.0f : m_new));
+          m_run[cg] = m_new;
+          l_run[cg] *= alpha;
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[cg][e] *= alpha;
         }
+      }
+      V8 pb[kCg];
+#pragma unroll
+      for (int cg = 0; cg < kCg; ++cg) {
+        const float neg_m = m_run[cg] == -INFINITY ? 0.0f : -m_run[cg];
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(z[cg][j], sl, neg_m));
+        if (masked) {
+          // masked keys give exp2(-inf) = 0, except at sl = 0 (NaN)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) p[j] = z[cg][j] == -INFINITY ? 0.0f : p[j];
+        }
+        l_run[cg] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         pb[cg] = __builtin_bit_cast(V8, make_uint4(M::pack2(p[0], p[1]), M::pack2(p[2], p[3]), M::pack2(p[4], p[5]),
                                                    M::pack2(p[6], p[7])));
       }
-      // A of MFMA e: element e (dims 8 * r16 + e) of the V rows of the
-      // lane's 8 key slots, two 16-bit values a dword, read per dword pair
+      // O^T += V^T . P, MFMA e over head dims 16e .. 16e + 15: A holds, for
+      // lane (m, g4), V of dim 16e + m at the lane's 8 key slots, which two
+      // transposing LDS reads deliver from the row-major tile (each lane
+      // names one 4-element row piece; see vt_off)
 #pragma unroll
-      for (int ep = 0; ep < 4; ++ep) {
-        uint32_t x[8];
+      for (int e = 0; e < 8; ++e) {
+        const uint8_t *vb = &s_v[buf][vt_off + 32 * e];
+        const uint2 lo = read_tr(vb), hi = read_tr(vb + 16 * kRowBytes);
+        const V8 va = __builtin_bit_cast(V8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int row = 16 * (j >> 2) + 4 * g4 + (j & 3);
-          x[j] = *reinterpret_cast<const uint32_t *>(&s_v[buf][row * kRowBytes + r16 * 16 + 4 * ep]);
-        }
-#pragma unroll
-        for (int eo = 0; eo < 2; ++eo) {
-          const uint32_t sel = eo ? 0x07060302u : 0x05040100u;
-          const V8 va = __builtin_bit_cast(V8, make_uint4(__builtin_amdgcn_perm(x[1], x[0], sel),
-                                                          __builtin_amdgcn_perm(x[3], x[2], sel),
-                                                          __builtin_amdgcn_perm(x[5], x[4], sel),
-                                                          __builtin_amdgcn_perm(x[7], x[6], sel)));
-#pragma unroll
-          for (int cg = 0; cg < kCg; ++cg) acc[cg][2 * ep + eo] = M::run(va, pb[cg], acc[cg][2 * ep + eo]);
-        }
+        for (int cg = 0; cg < kCg; ++cg) acc[cg][e] = M::run(va, pb[cg], acc[cg][e]);
       }
     };
 
@@ -343,19 +388,17 @@ struct Prefill {
       __syncthreads();
     }
 
+    // acc[cg][e][r] is dim 16e + 4 g4 + r of column r16
     const float nanv = __builtin_nanf("");
 #pragma unroll
     for (int cg = 0; cg < kCg; ++cg) {
       const float l = xor32_sum(xor16_sum(l_run[cg]));
       if (!valid[cg]) continue;
       const float mul = bad ? nanv : 1.0f / l;
-      const int64_t idx = out_idx(cg);
+      const int64_t idx = out_idx(cg) + 4 * g4;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        store4(a.out, idx + 8 * r4, make_float4(acc[cg][0][r4], acc[cg][1][r4], acc[cg][2][r4], acc[cg][3][r4]), mul);
-        store4(a.out, idx + 8 * r4 + 4, make_float4(acc[cg][4][r4], acc[cg][5][r4], acc[cg][6][r4], acc[cg][7][r4]),
-               mul);
-      }
+      for (int e = 0; e < 8; ++e)
+        store4(a.out, idx + 16 * e, make_float4(acc[cg][e][0], acc[cg][e][1], acc[cg][e][2], acc[cg][e][3]), mul);
     }
   }
 };
