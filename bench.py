@@ -81,7 +81,7 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-DECODE_SOURCES = ("pa_decode_fast.hip", "pa_common.h", "pa_internal.h")
+DECODE_SOURCES = ("pa_decode_fast.hip", "pa_common.h", "pa_internal.h", "pa_mfma.h")
 
 
 def recorded_traffic(partition):

@@ -257,6 +257,19 @@ def test_relabelled_blocks_give_identical_bits():
         assert torch.equal(x.view(torch.int16), y.view(torch.int16)), p
 
 
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+def test_negative_and_zero_scale(scale):
+    """Any finite scale, on the matrix-core path (single pass, balanced and
+    fixed splits) and the generic one."""
+    for kv, d in (("bf16", 128), ("bf16", 64)):
+        wl = W.build_decode(70, name="scale", q_dtype="bf16", kv_dtype=kv, num_q_heads=32, num_kv_heads=8,
+                            head_dim=d, block_size=16, num_blocks=600,
+                            context_lens=np.array([1, 17, 300, 1500, 2000], np.int32),
+                            rng=np.random.default_rng(70), poison=True)
+        wl.scale = scale
+        check_decode(wl, parts=(0, pa.PA_PARTITION_AUTO, 256), label=f"scale {scale} D={d}")
+
+
 def test_deterministic_repeats():
     wl = W.config2(seed=23, num_seqs=5, ctx_range=(100, 900), num_blocks=512)
     dev = DeviceWorkload(wl)

@@ -123,3 +123,20 @@ def test_prefill_bad_length_gives_nan_rows():
     assert np.isnan(got[qs[1]:qs[2]]).all()
     keep = np.r_[qs[0]:qs[1], qs[2]:qs[3]]
     assert max_err(got[keep], ref[keep]) <= 2e-2
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+@pytest.mark.parametrize("shape", [("bf16", "bf16", 32, 8, 128, 16), ("f16", "f16", 16, 8, 128, 32),
+                                   ("bf16", "bf16", 12, 4, 128, 16)])
+def test_prefill_negative_and_zero_scale(shape, scale):
+    """Any finite scale: a negative one reverses the softmax's preference
+    (the matrix-core kernel moves its sign onto q), zero gives the plain mean
+    of the attended V rows."""
+    qd, kd, hq, hkv, d, bs = shape
+    lens, qlens = [1, 40, 129, 300], [1, 40, 64, 33]
+    wl, q, qs = prefill_case(640 + hq, qd, kd, hq, hkv, d, bs, lens, qlens)
+    wl.scale = scale
+    got, ref, _, _ = run_case(wl, q, qs, window=0)
+    err = max_err(got, ref)
+    say(f"[prefill] {shape} scale {scale}: max abs err {err:.3e}")
+    assert np.isfinite(got).all() and err <= tol_for(wl), err
