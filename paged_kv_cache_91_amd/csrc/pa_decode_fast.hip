@@ -198,6 +198,7 @@ struct Fast {
   static_assert(BS % kTile == 0, "block size must be a multiple of 16");
   // K/V tiles in flight per wave (an fp8 tile carries half the bytes)
   static constexpr int kRing = kFp8 ? 4 : 2;
+  static constexpr int kKxBytes = kFp8 ? kTile * kRow : 16;     // LDS of k_relayout per wave
 
   // first head dim of chunk j's 8-element run for lane group g (A and B agree)
   static __device__ __forceinline__ int dbase(int j, int g) {
@@ -213,6 +214,7 @@ struct Fast {
   // Issue the loads of the tile whose 16 rows start at byte `off` of the K
   // and V pools (uniform), or loads that read nothing when !on.  ko / vo are
   // this lane's byte offsets inside a tile (lane_offsets()).
+  template <bool KW>
   static __device__ __forceinline__ void issue(Tile &t, const uint8_t *__restrict__ kb,
                                                const uint8_t *__restrict__ vb, int64_t off, bool on,
                                                int ko, int vo) {
@@ -220,21 +222,44 @@ struct Fast {
     const auto rk = tile_rsrc(kb + off, bytes);
     const auto rv = tile_rsrc(vb + off, bytes);
 #pragma unroll
-    for (int j = 0; j < (kFp8 ? 2 : 4); ++j) load_tile(rk, ko + 64 * j, t.k[j]);
+    for (int j = 0; j < (kFp8 ? 2 : 4); ++j) load_tile(rk, ko + (KW ? 1024 : 64) * j, t.k[j]);
 #pragma unroll
     for (int c = 0; c < 4; ++c) load_tile(rv, vo + c * kRow, t.v[c]);
   }
   // K: lane (r16, g4) reads row r16, 16 bytes at 16*g4 of every 64-byte
-  // chunk (the MFMA A slots, matching dbase); V: rows 4*g4 .. 4*g4+3, the
-  // 8 elements from 8*r16.
-  static __device__ __forceinline__ int k_lane_offset(int r16, int g4) { return r16 * kRow + 16 * g4; }
+  // chunk (the MFMA A slots, matching dbase).  An fp8 row is one 128-byte
+  // line, which that layout fetches in two halves; with KW (whole rows, fp8
+  // only) lane l reads bytes 16 l of each kilobyte instead (load j: rows
+  // 8j .. 8j + 7 whole) and k_relayout moves the chunks into the A slots.
+  // V: rows 4*g4 .. 4*g4+3, the 8 elements from 8*r16.
+  template <bool KW>
+  static __device__ __forceinline__ int k_lane_offset(int r16, int g4) {
+    static_assert(!KW || kFp8, "whole-row K loads are for fp8 rows");
+    return KW ? 16 * (r16 + 16 * g4) : r16 * kRow + 16 * g4;
+  }
+
+  // fp8 K from whole-row loads to the MFMA layout, through the wave's own
+  // 2 KiB of LDS (`kx`): lane (r16, g4) gets the 16-byte chunks g4 and g4 + 4
+  // of row r16 (dims 16 g4 .. + 15 and 64 + 16 g4 .. + 15, as dbase reads
+  // them).  Chunk c of row r sits at chunk c ^ ((r >> 1) & 7) of the row's
+  // 128 bytes, so the 16 rows read by one quarter of the wave fall on
+  // distinct banks.  A wave's LDS operations complete in order, so the slot
+  // is reused by the next tile without a wait.
+  static __device__ __forceinline__ void k_relayout(const Tile &t, uint8_t *kx, int lane, uint4 (&kk)[2]) {
+    auto at = [&](int row, int c) { return reinterpret_cast<uint4 *>(kx + row * 128 + 16 * (c ^ ((row >> 1) & 7))); };
+#pragma unroll
+    for (int j = 0; j < 2; ++j) *at(8 * j + (lane >> 3), lane & 7) = t.k[j];
+    const int r16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) kk[h] = *at(r16, g4 + 4 * h);
+  }
   static __device__ __forceinline__ int v_lane_offset(int r16, int g4) {
     return 4 * g4 * kRow + 8 * r16 * kEsz;
   }
 
-  static __device__ __forceinline__ V8 a_operand(const Tile &t, int j) {
+  static __device__ __forceinline__ V8 a_operand(const uint4 (&kk)[kFp8 ? 2 : 4], int j) {
     if constexpr (kFp8) {
-      const uint4 w = t.k[j >> 1];
+      const uint4 w = kk[j >> 1];
       const uint32_t lo = (j & 1) ? w.z : w.x;
       const uint32_t hi = (j & 1) ? w.w : w.y;
       uint4 r;
@@ -244,7 +269,7 @@ struct Fast {
       r.w = M::template from_fp8<true>(hi);
       return __builtin_bit_cast(V8, r);
     } else {
-      return __builtin_bit_cast(V8, t.k[j]);
+      return __builtin_bit_cast(V8, kk[j]);
     }
   }
 
@@ -305,13 +330,21 @@ struct Fast {
     }
   }
 
-  template <bool MASKED>
+  template <bool MASKED, bool KW>
   static __device__ __forceinline__ void compute(const Tile &t, const V8 (&qb)[4], int tpos, int pbeg,
                                                  int pend, int g4, float scale_log2,
-                                                 float &m_run, float &l_run, f32x4_t (&acc)[8]) {
+                                                 float &m_run, float &l_run, f32x4_t (&acc)[8],
+                                                 uint8_t *kx, int lane) {
+    uint4 kk[kFp8 ? 2 : 4];
+    if constexpr (KW) {
+      k_relayout(t, kx, lane, kk);
+    } else {
+#pragma unroll
+      for (int j = 0; j < (kFp8 ? 2 : 4); ++j) kk[j] = t.k[j];
+    }
     f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s = M::run(a_operand(t, j), qb[j], s);
+    for (int j = 0; j < 4; ++j) s = M::run(a_operand(kk, j), qb[j], s);
     const int p0 = tpos + 4 * g4;
     float sc[4];
 #pragma unroll
@@ -353,10 +386,14 @@ struct Fast {
       const DecodeArgs &a, const V8 (&qb)[4], const uint8_t *__restrict__ kb,
       const uint8_t *__restrict__ vb, const int32_t *__restrict__ trow, int pbeg, int pend, int t_first,
       int count, int stride, int r16, int g4, float &m_run, float &l_run, f32x4_t (&acc)[8],
-      bool &bad) {
+      bool &bad, uint8_t *kx) {
+    const int lane = r16 + 16 * g4;
     const int64_t blk_bytes = static_cast<int64_t>(BS) * kRow * a.num_kv_heads;
     const int jmax = (pend - 1) / BS;
-    const int ko = k_lane_offset(r16, g4), vo = v_lane_offset(r16, g4);
+    // fp8: whole-row K loads (measured faster here; the balanced split's
+    // stream keeps the half-row layout, which measured faster there)
+    constexpr bool KW = kFp8;
+    const int ko = k_lane_offset<KW>(r16, g4), vo = v_lane_offset(r16, g4);
     auto tpos = [&](int i) { return (t_first + stride * i) * kTile; };
     // raw table entry for tile i (clamped to the last block, so always readable)
     auto entry = [&](int i) { return load_const(trow, min(tpos(i) / BS, jmax)); };
@@ -366,7 +403,7 @@ struct Fast {
       const bool live = i < count;
       bad |= live && !valid;
       const int64_t off = (valid ? static_cast<int64_t>(e) * blk_bytes : 0) + tpos(i) % BS * kRow;
-      issue(t, kb, vb, off, live && valid, ko, vo);
+      issue<KW>(t, kb, vb, off, live && valid, ko, vo);
     };
 
     m_run = -INFINITY;
@@ -385,9 +422,9 @@ struct Fast {
         const int i = i0 + k;
         if (i < count) {
           if (tpos(i) + kTile <= pend && tpos(i) >= pbeg)
-            compute<false>(ring[k], qb, tpos(i), pbeg, pend, g4, a.scale_log2, m_run, l_run, acc);
+            compute<false, KW>(ring[k], qb, tpos(i), pbeg, pend, g4, a.scale_log2, m_run, l_run, acc, kx, lane);
           else
-            compute<true>(ring[k], qb, tpos(i), pbeg, pend, g4, a.scale_log2, m_run, l_run, acc);
+            compute<true, KW>(ring[k], qb, tpos(i), pbeg, pend, g4, a.scale_log2, m_run, l_run, acc, kx, lane);
         }
         __builtin_amdgcn_sched_barrier(0);
         const int e = e_next;
@@ -946,7 +983,7 @@ struct Fast {
     // Set-up order: the first table entry, the q loads, then the first
     // kRing tiles' loads, and only then the q stores to LDS (whose wait for
     // the q loads leaves the tile loads in flight).
-    const int ko = k_lane_offset(r16, g4), vo = v_lane_offset(r16, g4);
+    const int ko = k_lane_offset<false>(r16, g4), vo = v_lane_offset(r16, g4);
     const int64_t head_bytes = static_cast<int64_t>(BS) * kRow;
     const int64_t blk_bytes = head_bytes * a.num_kv_heads;
     const uint8_t *kpool = static_cast<const uint8_t *>(a.k_pool);
@@ -997,7 +1034,7 @@ struct Fast {
         if (gi + 1 < hi) e_next = entry_at(ci);
       }
       ++gi;
-      issue(tile, kpool, vpool, off, on, ko, vo);
+      issue<false>(tile, kpool, vpool, off, on, ko, vo);
     };
 
     Tile ring[kRing];
@@ -1052,9 +1089,9 @@ struct Fast {
           }
           const int tp = (cc.t0 + cc.t) * kTile;
           if (tp + kTile <= cc.n && tp >= cc.lo)
-            compute<false>(ring[k], qb, tp, cc.lo, cc.n, g4, a.scale_log2, m_run, l_run, acc);
+            compute<false, false>(ring[k], qb, tp, cc.lo, cc.n, g4, a.scale_log2, m_run, l_run, acc, nullptr, lane);
           else
-            compute<true>(ring[k], qb, tp, cc.lo, cc.n, g4, a.scale_log2, m_run, l_run, acc);
+            compute<true, false>(ring[k], qb, tp, cc.lo, cc.n, g4, a.scale_log2, m_run, l_run, acc, nullptr, lane);
           bad |= ((slot_bad >> k) & 1u) != 0;
 
           if (gc == hi - 1 || cc.t == cc.nts - 1) {
@@ -1410,6 +1447,7 @@ struct Fast {
   static __device__ void run_item(const DecodeArgs &a, int part, int y, int seq) {
     __shared__ float s_ml[NW][GT][2];
     __shared__ float4 s_acc[NW][GT][kHd / 4];
+    __shared__ __align__(16) uint8_t s_kx[NW][kKxBytes];       // fp8 K relayout, one slot per wave
 
     const int kvh = y / a.head_groups;
     const int hg = y - kvh * a.head_groups;
@@ -1456,7 +1494,7 @@ struct Fast {
     float m_run, l_run;
     f32x4_t acc[8];
     accumulate(a, qb, kb, vb, trow, pstart, pend, tfirst + wave, nloc, NW, r16, g4, m_run, l_run, acc,
-               bad);
+               bad, s_kx[wave]);
 
     // add the four row groups' sums of exponentials, then hand the wave's
     // state to LDS (lane (h, g4) holds dims 32*g4 .. +31 of head h)
