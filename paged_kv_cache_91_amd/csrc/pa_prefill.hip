@@ -52,6 +52,7 @@ constexpr int kKeys = 32;                  // keys per staged tile
 constexpr int kRowBytes = kHd * 2 + 32;
 constexpr int kWaves = 4;
 constexpr int kCg = 2;                     // column groups (16 columns each) per wave
+constexpr int kRsrcWord3 = 0x00020000;     // buffer resource: raw buffer, 32-bit elements
 constexpr float kLazy = 8.0f;              // base-2 headroom before the running max moves
 
 // IEEE maximum (NaN-propagating): v_maximum3_f32 on gfx950, with none of the
@@ -225,44 +226,54 @@ struct Prefill {
     const int32_t *trow = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
     const int jmin = klo / BS, jmax = (khi - 1) / BS;
     bool bad = false;
-    // byte offset of the 16-byte chunk of row rr of the 16 positions from
-    // kb16 (a multiple of 16, so all 16 sit in one block: the table entry is
-    // uniform and read with a scalar load)
-    auto offset_of = [&](int kb16) {
+    // The 16 positions from kb16 (a multiple of 16) sit in one block, so
+    // their table entry is uniform (a scalar load) and so is the address of
+    // their rows: a buffer resource over those 16 rows, with this thread's
+    // chunk at a fixed offset.
+    const int lane_off = rr * (kHd * 2) + ch * 16;
+    auto rows_of = [&](const uint8_t *pool, int kb16) {
       const int j = uniform(min(max(kb16 / BS, jmin), jmax));
       int e = load_const(trow, j);
       if (static_cast<uint32_t>(e) >= static_cast<uint32_t>(a.num_blocks)) {
         bad = true;
         e = 0;
       }
-      return static_cast<int64_t>(e) * blk_bytes + (kb16 % BS + rr) * (kHd * 2) + ch * 16;
+      const int64_t base = static_cast<int64_t>(e) * blk_bytes + (kb16 % BS) * (kHd * 2);
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(pool + base), 0, 16 * kHd * 2, kRsrcWord3);
+    };
+    auto load16 = [&](__amdgpu_buffer_rsrc_t r) {
+      typedef uint32_t w4 __attribute__((ext_vector_type(4)));
+      const w4 v = __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, 0, 0);
+      return make_uint4(v[0], v[1], v[2], v[3]);
     };
     // the next tile's chunks, held in named registers (an array here ends up
     // in scratch memory, which would wait for the loads at once)
     uint4 sk0, sk1, sv0, sv1;
     auto fetch = [&](int t) {
       const int kbase = uniform((kt0 + t) * kKeys);
-      const int64_t o0 = offset_of(kbase), o1 = offset_of(kbase + 16);
-      sk0 = *reinterpret_cast<const uint4 *>(kpool + o0);
-      sv0 = *reinterpret_cast<const uint4 *>(vpool + o0);
-      sk1 = *reinterpret_cast<const uint4 *>(kpool + o1);
-      sv1 = *reinterpret_cast<const uint4 *>(vpool + o1);
+      sk0 = load16(rows_of(kpool, kbase));
+      sv0 = load16(rows_of(vpool, kbase));
+      sk1 = load16(rows_of(kpool, kbase + 16));
+      sv1 = load16(rows_of(vpool, kbase + 16));
     };
     // V rows of positions outside [klo, khi) hold bytes of no position
     // attended here: their probabilities are 0, but NaN or Inf would survive
-    // the product, so they are staged as zeros
+    // the product, so on the tiles that reach outside they are staged as
+    // zeros (all-ones or all-zeros masks: a select of whole vectors becomes a
+    // scratch-memory lookup)
     auto stage = [&](int buf, int t) {
-      const int kbase = (kt0 + t) * kKeys;
-      // all-ones or all-zeros masks (a select of whole vectors becomes a
-      // scratch-memory lookup)
-      const uint32_t m0 = (kbase + rr >= klo && kbase + rr < khi) ? ~0u : 0u;
-      const uint32_t m1 = (kbase + rr + 16 >= klo && kbase + rr + 16 < khi) ? ~0u : 0u;
+      const int kbase = uniform((kt0 + t) * kKeys);
+      uint4 v0 = sv0, v1 = sv1;
+      if (kbase < klo || kbase + kKeys > khi) {
+        const uint32_t m0 = (kbase + rr >= klo && kbase + rr < khi) ? ~0u : 0u;
+        const uint32_t m1 = (kbase + rr + 16 >= klo && kbase + rr + 16 < khi) ? ~0u : 0u;
+        v0 = make_uint4(v0.x & m0, v0.y & m0, v0.z & m0, v0.w & m0);
+        v1 = make_uint4(v1.x & m1, v1.y & m1, v1.z & m1, v1.w & m1);
+      }
       *reinterpret_cast<uint4 *>(&s_k[buf][rr * kRowBytes + ch * 16]) = sk0;
-      *reinterpret_cast<uint4 *>(&s_v[buf][rr * kRowBytes + ch * 16]) =
-          make_uint4(sv0.x & m0, sv0.y & m0, sv0.z & m0, sv0.w & m0);
+      *reinterpret_cast<uint4 *>(&s_v[buf][rr * kRowBytes + ch * 16]) = v0;
       *reinterpret_cast<uint4 *>(&s_k[buf][(rr + 16) * kRowBytes + ch * 16]) = sk1;
-      *reinterpret_cast<uint4 *>(&s_v[buf][(rr + 16) * kRowBytes + ch * 16]) =
-          make_uint4(sv1.x & m1, sv1.y & m1, sv1.z & m1, sv1.w & m1);
+      *reinterpret_cast<uint4 *>(&s_v[buf][(rr + 16) * kRowBytes + ch * 16]) = v1;
     };
 
     // Transposing read (ds_read_b64_tr_b16): within each 16-lane block, lane
