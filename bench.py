@@ -27,9 +27,11 @@ Reported (one JSON line):
                stream_bracket_mean_us: events recorded on the stream around
                the whole call, for reference).  `traffic` is the HBM byte
                count per launch from the committed rocprofv3 counter runs
-               (profiles/decode_traffic.json), reported only while the decode
+               (profiles/decode_traffic.json: the L2-to-memory read and write
+               requests counted by size), reported only while the decode
                kernel's source hash matches the one they were taken on;
-               `traffic_source` names the file and the counter scale factors;
+               `traffic_source` names the file, the request counts and the
+               copy-calibrated FETCH_SIZE/WRITE_SIZE figure beside them;
   cpu_baseline the float64 oracle (write + decode) on the same batch, on this
                host's cores (skipped with --no-cpu-baseline).
 """
@@ -102,8 +104,9 @@ def recorded_traffic(partition):
     if rec.get("kernel_source_sha256") != h.hexdigest() or rec.get("partition_size") != partition:
         return None, None
     src = {"kind": "recorded, not measured in this run", "file": "profiles/decode_traffic.json"}
-    src.update({k: rec[k] for k in ("fetch_kib_per_launch", "write_kib_per_launch", "fetch_scale",
-                                    "write_scale", "calibration") if k in rec})
+    src.update({k: rec[k] for k in ("method", "read_requests_per_launch", "write_requests_per_launch",
+                                    "fetch_kib_per_launch", "write_kib_per_launch", "fetch_scale",
+                                    "write_scale", "calibration", "calibrated_bytes_per_launch") if k in rec})
     return rec.get("hbm_bytes_per_launch"), src
 
 
