@@ -53,6 +53,7 @@ constexpr int kRowBytes = kHd * 2 + 32;
 constexpr int kWaves = 4;
 constexpr int kCg = 2;                     // column groups (16 columns each) per wave
 constexpr int kRsrcWord3 = 0x00020000;     // buffer resource: raw buffer, 32-bit elements
+constexpr int kMfmaPrio = 1;              // wave priority during the matrix-core bursts (measured: 2 gains nothing)
 constexpr float kLazy = 8.0f;              // base-2 headroom before the running max moves
 
 // IEEE maximum (NaN-propagating): v_maximum3_f32 on gfx950, with none of the
@@ -298,8 +299,9 @@ struct Prefill {
     // columns.  q.K^T runs per 16-key half (A = 16 key rows); lane (r16, g4)
     // then holds, for its column r16, the keys of slots j < 8: half j / 4,
     // key 4 * g4 + j % 4 -- exactly the K-slot order of a 16x16x32 MFMA, so
-    // P.V is eight 16x16x32 MFMAs over all 32 keys (A = V restricted to dims
-    // 8i + e in the same slot order, B = the probabilities in place).
+    // P.V is eight 16x16x32 MFMAs over all 32 keys (MFMA e: A = V of head
+    // dims 16e .. 16e + 15 in the same slot order, B = the probabilities in
+    // place).
     //
     // Online softmax in the base-2 domain, updated once per tile.  The
     // running max m of a column is only moved (and acc, l rescaled) when the
@@ -309,6 +311,9 @@ struct Prefill {
     // operand's range and with the same relative rounding.
     auto tile = [&](int buf, int kbase, bool masked) {
       float z[kCg][8];                 // raw dot products
+      // the matrix-core bursts run at raised wave priority, so that a wave
+      // entering one is issued ahead of the softmax work of the others
+      __builtin_amdgcn_s_setprio(kMfmaPrio);
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         V8 ka[4];
@@ -324,6 +329,7 @@ struct Prefill {
           for (int r4 = 0; r4 < 4; ++r4) z[cg][4 * hh + r4] = sc[r4];
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       // causal and window masks, on tiles that reach past a column's position
       // or start before its window (one uniform branch)
       if (masked) {
@@ -378,6 +384,7 @@ struct Prefill {
       // lane (m, g4), V of dim 16e + m at the lane's 8 key slots, which two
       // transposing LDS reads deliver from the row-major tile (each lane
       // names one 4-element row piece; see vt_off)
+      __builtin_amdgcn_s_setprio(kMfmaPrio);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint8_t *vb = &s_v[buf][vt_off + 32 * e];
@@ -386,6 +393,7 @@ struct Prefill {
 #pragma unroll
         for (int cg = 0; cg < kCg; ++cg) acc[cg][e] = M::run(va, pb[cg], acc[cg][e]);
       }
+      __builtin_amdgcn_s_setprio(0);
     };
 
     fetch(0);
