@@ -1,11 +1,12 @@
-"""Code-generation guard for the balanced-split decode kernel (CPU only).
+"""Code-generation guards for the head-dim-128 kernels (CPU only): the
+balanced-split decode kernel's schedule, and the prefill kernels' registers.
 
 The streaming wave keeps two K/V tiles (16 loads) in flight while it computes
 the current one.  That depends on the tile loop's cursor staying in scalar
 registers: once the compiler treats it as per-lane, table entries and
 context lengths become vector loads, and each such load waits for every
 tile load issued before it, which cost a third of the kernel's speed once.
-This test compiles the head-dim-128 kernels to gfx950 assembly and checks
+The first tests compile the decode kernels to gfx950 assembly and check
 the signature of the intended schedule in decode_pair_kernel<bf16, bf16,
 group 4, block 16>, the kernel the Llama-3-8B-shaped layer runs:
 
@@ -50,3 +51,36 @@ def test_tile_loop_keeps_two_tiles_in_flight(pair_isa):
 def test_tile_loop_reads_tables_and_lengths_with_scalar_loads(pair_isa):
     vector_dword_loads = len(re.findall(r"\bglobal_load_dword\s", pair_isa))
     assert vector_dword_loads <= 8, vector_dword_loads
+
+
+# Prefill: the prefetched K/V chunks once went through scratch memory (an
+# array in a lambda), which also made every tile wait for its loads at once,
+# and register growth past 168 drops the kernel from three waves per SIMD to
+# two (both measured several percent).  Every prefill specialisation must
+# compile with no scratch and at most 168 VGPRs.
+PREFILL_MAX_VGPRS = 168
+
+
+@pytest.fixture(scope="module")
+def prefill_resources(tmp_path_factory):
+    out = tmp_path_factory.mktemp("isa") / "pf.o"
+    cmd = [B.hipcc(), *B.FLAGS, "--cuda-device-only", "-c", os.path.join(B.PKG, "csrc", "pa_prefill.hip"),
+           "-o", str(out), "-Rpass-analysis=kernel-resource-usage"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        pytest.skip("hipcc unavailable: " + res.stderr[-300:])
+    kernels = {}
+    for block in res.stderr.split("Function Name: ")[1:]:
+        name = block.split()[0]
+        vgpr = int(re.search(r"VGPRs: (\d+)", block).group(1))
+        scratch = int(re.search(r"ScratchSize \[bytes/lane\]: (\d+)", block).group(1))
+        kernels[name] = (vgpr, scratch)
+    return kernels
+
+
+def test_prefill_kernels_keep_three_waves_per_simd_without_scratch(prefill_resources):
+    pf = {k: v for k, v in prefill_resources.items() if "prefill_kernel" in k}
+    assert len(pf) == 16, sorted(pf)                    # bf16/f16 x block 16/32 x group 1/2/4/8
+    for name, (vgpr, scratch) in pf.items():
+        assert scratch == 0, (name, scratch)
+        assert vgpr <= PREFILL_MAX_VGPRS, (name, vgpr)
