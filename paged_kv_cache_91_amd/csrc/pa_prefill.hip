@@ -25,9 +25,9 @@
 //                   keys 4*(l/16)+r of each half for column l%16;
 //   online softmax per column in the base-2 domain over the 32 keys, causal
 //   (and window) mask only on tiles that reach past a column's position;
-//   O^T += V^T . P  eight v_mfma_f32_16x16x32 over all 32 keys (A = V rows
-//                   from LDS repacked with v_perm into the probabilities'
-//                   key order, B = the probabilities in place).
+//   O^T += V^T . P  eight v_mfma_f32_16x16x32 over all 32 keys (A = V read
+//                   from the row-major tile by transposing LDS reads in the
+//                   probabilities' key order, B = the probabilities in place).
 // Blocks are ordered so that all blocks of one (sequence, KV head) land on
 // one XCD (their K/V is re-read from that XCD's L2), last block first.
 
