@@ -602,10 +602,48 @@ def pin_swap(ora):
     assert np.array_equal(a, b)
 
 
+def pin_any_scale(ora):
+    """The scale is any finite number: a negative one matches torch SDPA with
+    that scale (decode and causal prefill); zero gives every attended key the
+    same weight, so each output is the plain mean of the attended V rows."""
+    lens = [1, 6, 17, 40]
+    hq, hkv, d, bs = 6, 2, 8, 4
+    q, k_seq, v_seq, tables, nblocks = _random_paged(41, lens, hq, hkv, d, bs)
+    kp, vp = _place_contiguous(k_seq, v_seq, tables, nblocks, bs)
+    neg = np.float32(-0.45)
+    out = ora.oracle_decode(q, "f32", kp, vp, "f32", tables, np.array(lens), neg)
+    for s in range(len(lens)):
+        ref = _sdpa64(q[s], k_seq[s], v_seq[s], hq // hkv, float(neg))
+        assert np.max(np.abs(out[s] - ref)) <= 1e-12
+    zero = ora.oracle_decode(q, "f32", kp, vp, "f32", tables, np.array(lens), 0.0)
+    for s in range(len(lens)):
+        mean = np.repeat(v_seq[s].astype(np.float64).mean(axis=1), hq // hkv, axis=0)
+        assert np.max(np.abs(zero[s] - mean)) <= 1e-12
+    # causal prefill with a negative scale, and a window at scale 0
+    q2, k_seq, v_seq, tables, kp, vp, qs = _prefill_case(42, lens, lens, hq, hkv, d, bs)
+    out = ora.oracle_prefill(q2, "f32", kp, vp, "f32", tables, np.array(lens), qs, neg)
+    for s, n in enumerate(lens):
+        qt = torch.from_numpy(q2[qs[s]:qs[s + 1]].astype(np.float64)).permute(1, 0, 2)[None]
+        kt = torch.from_numpy(k_seq[s].astype(np.float64)).repeat_interleave(3, dim=0)[None]
+        vt = torch.from_numpy(v_seq[s].astype(np.float64)).repeat_interleave(3, dim=0)[None]
+        # the causal mask as an explicit boolean mask: torch's is_causal path
+        # takes the square root of the scale and gives NaN for a negative one
+        mask = torch.ones(n, n, dtype=torch.bool).tril()
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=float(neg))
+        assert np.max(np.abs(out[qs[s]:qs[s + 1]] - ref[0].permute(1, 0, 2).numpy())) <= 1e-12
+    W = 5
+    win = ora.oracle_prefill(q2, "f32", kp, vp, "f32", tables, np.array(lens), qs, 0.0, window=W)
+    for s, n in enumerate(lens):
+        v64 = np.repeat(v_seq[s].astype(np.float64), hq // hkv, axis=0)      # [Hq, n, D]
+        for i, p in enumerate(range(n)):
+            mean = v64[:, max(0, p + 1 - W):p + 1].mean(axis=1)
+            assert np.max(np.abs(win[qs[s] + i] - mean)) <= 1e-12
+
+
 ALL_PINS = [
     pin_ul_pool_example, pin_zc_trace, pin_block_counts, pin_pool_sizing, pin_pd_scalar,
     pin_closed_forms, pin_zero_length, pin_bruteforce, pin_sdpa, pin_bf16_f16_decoding,
     pin_relabel_invariance, pin_split_merge, pin_fp8_table, pin_fp8_encode,
     pin_fp8_write_decode, pin_write_copy, pin_window_decode, pin_prefill, pin_prefill_relabel,
-    pin_swap,
+    pin_swap, pin_any_scale,
 ]

@@ -49,6 +49,10 @@ MUTANTS = [
     ("prefill-group", "kvh = h // group\n                z = scale64 * (k[kvh, lo",
      "kvh = h % num_kv_heads\n                z = scale64 * (k[kvh, lo"),
     ("swap-direction", "dst_k[dst] = src_k[src]", "dst_k[dst] = dst_k[src]"),
+    ("decode-scale-magnitude", "    scale64 = float(np.float32(scale))\n    qf = to_float64(q, q_dtype)\n    out = np.zeros((num_seqs,",
+     "    scale64 = abs(float(np.float32(scale)))\n    qf = to_float64(q, q_dtype)\n    out = np.zeros((num_seqs,"),
+    ("prefill-scale-magnitude", "    scale64 = float(np.float32(scale))\n    qf = to_float64(q, q_dtype)\n    out = np.zeros((num_tokens,",
+     "    scale64 = abs(float(np.float32(scale)))\n    qf = to_float64(q, q_dtype)\n    out = np.zeros((num_tokens,"),
 ]
 
 
