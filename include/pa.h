@@ -246,7 +246,11 @@ int pa_decode_window(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t n
  *                 lengths (n outside [0, max_blocks_per_seq * bs], L > n) are
  *                 NaN.
  *   query_start   device, int32 [num_seqs + 1], nondecreasing, query_start[0]
- *                 = 0 and query_start[num_seqs] = num_tokens.
+ *                 = 0 and query_start[num_seqs] = num_tokens.  Entries that
+ *                 break these rules never make the call read q or write out
+ *                 outside their num_tokens rows; the rows of the sequences
+ *                 they spoil hold NaN, keep their old value or hold
+ *                 meaningless numbers.
  *   window        >= 0; 0 attends every earlier position.
  * q_dtype / pool dtype combinations, head dims, block sizes, block_tables,
  * context_lens and scale are as for pa_decode.  No workspace is needed.

@@ -129,7 +129,7 @@ struct Prefill {
         uint32_t nb = 0;
         if (s < S) {
           const int L = a.query_start[s + 1] - a.query_start[s];
-          nb = L > 0 ? static_cast<uint32_t>((L + kQb - 1) / kQb) : 0u;
+          nb = L > 0 ? static_cast<uint32_t>((static_cast<int64_t>(L) + kQb - 1) / kQb) : 0u;
         }
         const uint32_t incl = wave_incl_sum(nb);
         const int64_t total = __builtin_amdgcn_readlane(incl, 63);
@@ -144,7 +144,10 @@ struct Prefill {
         base += total;
       }
     }
-    if (seq < 0) return;                        // past the batch's blocks (the grid is an upper bound)
+    // past the batch's blocks (the grid is an upper bound); a block index
+    // outside its sequence's count only comes from a malformed prefix sum
+    // whose block counts wrapped the 32-bit scan
+    if (seq < 0 || k_in < 0 || k_in >= nb_s) return;
 
     const int q0 = load_const(a.query_start, seq);
     const int L = load_const(a.query_start, seq + 1) - q0;
@@ -153,7 +156,10 @@ struct Prefill {
     const int P0 = n - L;                                       // the first query's position
     const int pb0 = P0 + qb * kQb;                              // this block's first query position
     const int pb1 = min(n, pb0 + kQb);                          // one past its last
-    const bool bad_len = n < 0 || n > maxn || L > n;
+    // a malformed prefix sum (rows outside [0, num_tokens)) or length gives
+    // NaN rows; only rows inside out are ever written
+    const bool bad_rows = q0 < 0 || q0 + L > a.num_tokens;
+    const bool bad_len = bad_rows || n < 0 || n > maxn || L > n;
 
     // this lane's column in each column group: position qp[cg], head h
     const int h = kvh * G + r16 % G;
@@ -170,11 +176,15 @@ struct Prefill {
     if (bad_len) {
       const float nanv = __builtin_nanf("");
 #pragma unroll
-      for (int cg = 0; cg < kCg; ++cg)
-        if (valid[cg] && qp[cg] >= pb0)
+      for (int cg = 0; cg < kCg; ++cg) {
+        const int64_t row =
+            static_cast<int64_t>(q0) + static_cast<int64_t>(qb) * kQb + (wave * kCg + cg) * kPos + r16 / G;
+        if (row < static_cast<int64_t>(q0) + L && row >= 0 && row < a.num_tokens)
 #pragma unroll
           for (int r4 = 0; r4 < 8; ++r4)
-            store4(a.out, out_idx(cg) + 32 * g4 + 4 * r4, make_float4(nanv, nanv, nanv, nanv), 1.0f);
+            store4(a.out, (row * a.num_q_heads + h) * kHd + 32 * g4 + 4 * r4, make_float4(nanv, nanv, nanv, nanv),
+                   1.0f);
+      }
       return;
     }
 

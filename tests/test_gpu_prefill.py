@@ -140,3 +140,40 @@ def test_prefill_negative_and_zero_scale(shape, scale):
     err = max_err(got, ref)
     say(f"[prefill] {shape} scale {scale}: max abs err {err:.3e}")
     assert np.isfinite(got).all() and err <= tol_for(wl), err
+
+
+@pytest.mark.parametrize("shape", [("bf16", "bf16", 32, 8, 128, 16), ("bf16", "bf16", 12, 4, 128, 16)],
+                         ids=["matrix-cores", "vector"])
+@pytest.mark.parametrize("bad", ["past-end", "negative-start", "decreasing", "huge-last"])
+def test_prefill_malformed_query_start_stays_inside_out(shape, bad):
+    """A query_start that breaks its rules must not make the call write
+    outside out's num_tokens rows: out is a view inside a larger buffer whose
+    guard rows must keep their value.  Sequences the malformed entries do not
+    touch still match the oracle; the matrix-core kernel gives NaN for the
+    rows it can place of a sequence that leaves [0, num_tokens)."""
+    qd, kd, hq, hkv, d, bs = shape
+    lens, qlens = [40, 60, 50], [10, 20, 5]
+    wl, q, qs = prefill_case(650 + hq, qd, kd, hq, hkv, d, bs, lens, qlens)
+    T = len(q)
+    bad_qs = {"past-end": [0, 10, 30, 45], "negative-start": [-8, 10, 30, 35],
+              "decreasing": [0, 25, 10, 35], "huge-last": [0, 10, 30, 2**31 - 1]}[bad]
+    clean = {"past-end": [0, 1], "negative-start": [1, 2], "decreasing": [], "huge-last": [0, 1]}[bad]
+    dev = DeviceWorkload(wl)
+    qd_t = to_dev(q, qd)
+    guard = 64
+    buf = torch.full((guard + T + guard, hq, d), 3.0, dtype=qd_t.dtype, device=DEV)
+    out = buf[guard:guard + T]
+    say(f"[prefill] malformed query_start {bad} {shape}")
+    pa.pa_prefill(qd_t, dev.pool, dev.tables, dev.ctx, torch.tensor(bad_qs, dtype=torch.int32, device=DEV),
+                  wl.scale, out=out)
+    torch.cuda.synchronize()
+    host = buf.float().cpu().numpy()
+    assert (host[:guard] == 3.0).all() and (host[guard + T:] == 3.0).all()
+    got = host[guard:guard + T].astype(np.float64)
+    ref = oracle.oracle_prefill(q, qd, wl.k_pool, wl.v_pool, kd, wl.block_tables, wl.context_lens, qs, wl.scale)
+    for s in clean:
+        rows = slice(qs[s], qs[s + 1])
+        assert max_err(got[rows], ref[rows]) <= tol_for(wl), (s, bad)
+    if hq // hkv == 4 and bad in ("past-end", "negative-start"):
+        s = 2 if bad == "past-end" else 0
+        assert np.isnan(got[max(bad_qs[s], 0):min(bad_qs[s + 1], T)]).all()
