@@ -147,6 +147,21 @@ __device__ __forceinline__ void fold(const Partial &x, float &big_m, float &l, f
   }
   big_m = nm;
 }
+// fold() for four dims
+__device__ __forceinline__ void fold4(f32x2_t ml, f32x4_t x, float &big_m, float &l, float (&o)[4],
+                                      bool &nan_seen) {
+  const float m = ml[0];
+  nan_seen |= (m != m);
+  const float nm = fmaxf(big_m, m);
+  const float c_old = __builtin_amdgcn_exp2f(big_m - nm);
+  const float c_new = __builtin_amdgcn_exp2f(m - nm);
+  l = l * c_old + ml[1] * c_new;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = o[e] * c_old + x[e] * c_new;
+  big_m = nm;
+}
+// lane groups of 32 in the split's merge (up to 8 per workgroup)
+constexpr int kMergeGroups = 8;
 
 
 
@@ -198,7 +213,14 @@ struct Fast {
   static_assert(BS % kTile == 0, "block size must be a multiple of 16");
   // K/V tiles in flight per wave (an fp8 tile carries half the bytes)
   static constexpr int kRing = kFp8 ? 4 : 2;
+  // the ring of accumulate(): the split's one-wave workgroups run three
+  // waves per SIMD, so each keeps one fp8 tile less in flight (the 16
+  // registers it frees make room for the third wave)
+  static constexpr int kAccRing = (NW == 1 && kFp8) ? 3 : kRing;
   static constexpr int kKxBytes = kFp8 ? kTile * kRow : 16;     // LDS of k_relayout per wave
+  // how far (log2 units) a tile's maximum may pass the running maximum
+  // before the accumulators are rescaled
+  static constexpr float kLazy = 8.0f;
 
   // first head dim of chunk j's 8-element run for lane group g (A and B agree)
   static __device__ __forceinline__ int dbase(int j, int g) {
@@ -278,24 +300,19 @@ struct Fast {
   // selector 0x05040100 takes the low 16 bits of two dwords, 0x07060302 the
   // high 16 bits.  fp8 rows are first transposed bytewise (four rows' codes
   // of one dim into one dword) and then widened exactly to the MFMA type.
-  template <bool MASKED>
   static __device__ __forceinline__ void pv(const Tile &t, const uint32_t pb_lo, const uint32_t pb_hi,
-                                            int p0, int pbeg, int pend, f32x4_t (&acc)[8]) {
+                                            f32x4_t (&acc)[8]) {
     using V4 = typename M::V4;
     const V4 pb = __builtin_bit_cast(V4, make_uint2(pb_lo, pb_hi));
     auto mma = [&](int e, uint32_t a01, uint32_t a23) {
       acc[e] = M::run16(__builtin_bit_cast(V4, make_uint2(a01, a23)), pb, acc[e]);
     };
-    // rows outside [pbeg, pend) (past the context end, or before a sliding
-    // window) have p = 0, but their bytes may hold NaN or Inf, so they are
-    // zeroed before the product
-    auto keep = [&](int c) { return !MASKED || (p0 + c < pend && p0 + c >= pbeg); };
     if constexpr (kFp8) {
       uint32_t x[4][2];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        x[c][0] = keep(c) ? t.v[c].x : 0u;
-        x[c][1] = keep(c) ? t.v[c].y : 0u;
+        x[c][0] = t.v[c].x;
+        x[c][1] = t.v[c].y;
       }
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
@@ -315,10 +332,10 @@ struct Fast {
       uint32_t x[4][4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        x[c][0] = keep(c) ? t.v[c].x : 0u;
-        x[c][1] = keep(c) ? t.v[c].y : 0u;
-        x[c][2] = keep(c) ? t.v[c].z : 0u;
-        x[c][3] = keep(c) ? t.v[c].w : 0u;
+        x[c][0] = t.v[c].x;
+        x[c][1] = t.v[c].y;
+        x[c][2] = t.v[c].z;
+        x[c][3] = t.v[c].w;
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -330,11 +347,33 @@ struct Fast {
     }
   }
 
-  template <bool MASKED, bool KW>
-  static __device__ __forceinline__ void compute(const Tile &t, const V8 (&qb)[4], int tpos, int pbeg,
-                                                 int pend, int g4, float scale_log2,
+  // One tile: q.K^T, the online softmax, P.V.  `masked` (uniform): some of
+  // the tile's rows lie outside [pbeg, pend) (past the context end, or
+  // before a sliding window's first position); their scores become -inf and
+  // their V rows, whose bytes may hold NaN or Inf, are zeroed in place
+  // before the product.  Only inputs change under the branch, so the
+  // accumulators keep one set of registers (a masked and an unmasked copy
+  // of the whole tile made the compiler move them between two sets on
+  // every tile).
+  template <bool KW>
+  static __device__ __forceinline__ void compute(Tile &t, const V8 (&qb)[4], int tpos, int pbeg, int pend,
+                                                 bool masked, int g4, float scale_log2,
                                                  float &m_run, float &l_run, f32x4_t (&acc)[8],
                                                  uint8_t *kx, int lane) {
+    const int p0 = tpos + 4 * g4;
+    auto keep = [&](int c) { return p0 + c < pend && p0 + c >= pbeg; };
+    if (masked) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bool k = keep(c);
+        t.v[c].x = k ? t.v[c].x : 0u;
+        t.v[c].y = k ? t.v[c].y : 0u;
+        if constexpr (!kFp8) {
+          t.v[c].z = k ? t.v[c].z : 0u;
+          t.v[c].w = k ? t.v[c].w : 0u;
+        }
+      }
+    }
     uint4 kk[kFp8 ? 2 : 4];
     if constexpr (KW) {
       k_relayout(t, kx, lane, kk);
@@ -345,29 +384,33 @@ struct Fast {
     f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) s = M::run(a_operand(kk, j), qb[j], s);
-    const int p0 = tpos + 4 * g4;
     float sc[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sc[r] = s[r] * scale_log2;
-      if constexpr (MASKED) sc[r] = (p0 + r < pend && p0 + r >= pbeg) ? sc[r] : -INFINITY;
-    }
-    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mx = xor32_max(xor16_max(mx));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float p[4];
+    for (int r = 0; r < 4; ++r) sc[r] = s[r] * scale_log2;
+    if (masked) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sc[r] - m_new);
-    l_run = fmaf(l_run, alpha, (p[0] + p[1]) + (p[2] + p[3]));
-    m_run = m_new;
-    // rescale the accumulators (this lane's head's) only when some head's
-    // maximum moved
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+      for (int r = 0; r < 4; ++r) sc[r] = keep(r) ? sc[r] : -INFINITY;
+    }
+    float mx = max2(max2(sc[0], sc[1]), max2(sc[2], sc[3]));
+    mx = xor32_max(xor16_max(mx));
+    // Lazy running maximum: the exponentials are taken against m_run, which
+    // moves (rescaling l and the accumulators of this lane's head) only when
+    // some head's tile maximum passes it by more than kLazy.  Any reference
+    // value gives the same softmax (the shift cancels between O and l); one
+    // that trails the true maximum by at most kLazy keeps p <= 2^kLazy.
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+      m_run = m_new;
     }
-    pv<MASKED>(t, M::pack2(p[0], p[1]), M::pack2(p[2], p[3]), p0, pbeg, pend, acc);
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sc[r] - m_run);
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);
+    pv(t, M::pack2(p[0], p[1]), M::pack2(p[2], p[3]), acc);
   }
 
   // Accumulate `count` tiles of one (sequence, head group) into this wave's
@@ -375,8 +418,8 @@ struct Fast {
   // positions starting at 16 * tile; positions outside [pbeg, pend) are
   // masked.
   //
-  // The tiles stream through a ring of kRing buffers: the loads of tile
-  // i + kRing are issued as soon as tile i has been computed, so kRing
+  // The tiles stream through a ring of kAccRing buffers: the loads of tile
+  // i + kAccRing are issued as soon as tile i has been computed, so kAccRing
   // tiles are in flight while one is computed.  Every step issues loads
   // (switched off past the last tile), and a scheduling barrier keeps each
   // buffer's new loads after the compute that frees it, so the buffers stay
@@ -412,24 +455,22 @@ struct Fast {
     for (int e = 0; e < 8; ++e) acc[e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     if (count <= 0) return;
 
-    Tile ring[kRing];
+    Tile ring[kAccRing];
 #pragma unroll
-    for (int k = 0; k < kRing; ++k) issue_tile(ring[k], k, entry(k));
-    int e_next = entry(kRing);
-    for (int i0 = 0; i0 < count; i0 += kRing) {
+    for (int k = 0; k < kAccRing; ++k) issue_tile(ring[k], k, entry(k));
+    int e_next = entry(kAccRing);
+    for (int i0 = 0; i0 < count; i0 += kAccRing) {
 #pragma unroll
-      for (int k = 0; k < kRing; ++k) {
+      for (int k = 0; k < kAccRing; ++k) {
         const int i = i0 + k;
         if (i < count) {
-          if (tpos(i) + kTile <= pend && tpos(i) >= pbeg)
-            compute<false, KW>(ring[k], qb, tpos(i), pbeg, pend, g4, a.scale_log2, m_run, l_run, acc, kx, lane);
-          else
-            compute<true, KW>(ring[k], qb, tpos(i), pbeg, pend, g4, a.scale_log2, m_run, l_run, acc, kx, lane);
+          const bool masked = !(tpos(i) + kTile <= pend && tpos(i) >= pbeg);
+          compute<KW>(ring[k], qb, tpos(i), pbeg, pend, masked, g4, a.scale_log2, m_run, l_run, acc, kx, lane);
         }
         __builtin_amdgcn_sched_barrier(0);
         const int e = e_next;
-        e_next = entry(i + kRing + 1);
-        issue_tile(ring[k], i + kRing, e);
+        e_next = entry(i + kAccRing + 1);
+        issue_tile(ring[k], i + kAccRing, e);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -1088,10 +1129,8 @@ struct Fast {
             bad = false;
           }
           const int tp = (cc.t0 + cc.t) * kTile;
-          if (tp + kTile <= cc.n && tp >= cc.lo)
-            compute<false, false>(ring[k], qb, tp, cc.lo, cc.n, g4, a.scale_log2, m_run, l_run, acc, nullptr, lane);
-          else
-            compute<true, false>(ring[k], qb, tp, cc.lo, cc.n, g4, a.scale_log2, m_run, l_run, acc, nullptr, lane);
+          const bool masked = !(tp + kTile <= cc.n && tp >= cc.lo);
+          compute<false>(ring[k], qb, tp, cc.lo, cc.n, masked, g4, a.scale_log2, m_run, l_run, acc, nullptr, lane);
           bad |= ((slot_bad >> k) & 1u) != 0;
 
           if (gc == hi - 1 || cc.t == cc.nts - 1) {
@@ -1555,12 +1594,17 @@ struct Fast {
     }
   }
 
-  // The split's merge: workgroup (unit, j) of 64 lanes folds the partials of
-  // query heads 2j and 2j + 1 of that (sequence, head group) in increasing
-  // partition order (lanes 0-31 and 32-63, four dimensions a lane), eight
-  // partitions' loads in flight at a time.  Sequences held by one partition
-  // were written out by the partition itself.
-  static __device__ void run_merge(const DecodeArgs &a) {
+  // The split's merge: workgroup (unit, h) folds the partials of query head
+  // h of that (sequence, head group).  Its lanes form ng groups of 32 (four
+  // dims a lane); group j folds partitions j, j + ng, j + 2 ng, ... in
+  // increasing order, all of a round's loads (up to 8 partitions) in flight,
+  // and group 0 then folds the groups' states in group order.  The round
+  // count, not the bytes, sets the time: one round per 8 * ng partitions
+  // instead of one per 8.  Sequences held by one partition were written out
+  // by the partition itself.
+  static __device__ void run_merge(const DecodeArgs &a, int ng) {
+    __shared__ f32x4_t s_o[kMergeGroups][32];
+    __shared__ f32x2_t s_ml[kMergeGroups];
     const int64_t unit = blockIdx.x;
     const int KVG = a.num_kv_heads * a.head_groups;
     const int seq = static_cast<int>(unit / KVG);
@@ -1572,28 +1616,40 @@ struct Fast {
     const int P = a.partition_size;
     const int nparts = (n + P - 1) / P - window_lo(n, a.window) / P;
     if (nparts <= 1) return;
-    const int h = 2 * static_cast<int>(blockIdx.y) + (threadIdx.x >> 5);
+    const int h = static_cast<int>(blockIdx.y);
     const int hcount = min(GT, a.group - hg * GT);
     if (h >= hcount) return;
+    const int g = static_cast<int>(threadIdx.x >> 5);
     const int d4 = threadIdx.x & 31;
     const int64_t row0 = static_cast<int64_t>(seq) * a.num_q_heads + kvh * a.group + hg * GT;
     const float *bo = a.part_o + unit * a.max_parts * (GT * kHd) + h * kHd + 4 * d4;
     const float *bml = a.part_m + unit * a.max_parts * (GT * 2) + 2 * h;
-    float big_m = -INFINITY, l = 0.0f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float big_m = -INFINITY, l = 0.0f, o[4] = {0, 0, 0, 0};
     bool nan_seen = false;
-    for (int p0 = 0; p0 < nparts; p0 += 8) {
-      Partial x[8];
+    for (int p0 = g; p0 < nparts; p0 += 8 * ng) {
+      f32x2_t ml[8];
+      f32x4_t ov[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int pp = min(p0 + k, nparts - 1);
-        x[k].ml = *reinterpret_cast<const f32x2_t *>(bml + pp * GT * 2);
-        x[k].o0 = *reinterpret_cast<const f32x4_t *>(bo + pp * GT * kHd);
-        x[k].o1 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        const int pp = min(p0 + k * ng, nparts - 1);
+        ml[k] = *reinterpret_cast<const f32x2_t *>(bml + pp * GT * 2);
+        ov[k] = *reinterpret_cast<const f32x4_t *>(bo + pp * GT * kHd);
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        if (p0 + k < nparts) fold(x[k], big_m, l, o, nan_seen);
+        if (p0 + k * ng < nparts) fold4(ml[k], ov[k], big_m, l, o, nan_seen);
     }
+    // groups 0 .. min(ng, nparts) - 1 hold at least one partition each
+    s_o[g][d4] = f32x4_t{o[0], o[1], o[2], o[3]};
+    if (d4 == 0) s_ml[g] = f32x2_t{nan_seen ? __builtin_nanf("") : big_m, l};
+    __syncthreads();
+    if (g != 0) return;
+    const int used = min(ng, nparts);
+    big_m = -INFINITY;
+    l = 0.0f;
+    o[0] = o[1] = o[2] = o[3] = 0.0f;
+    nan_seen = false;
+    for (int j = 0; j < used; ++j) fold4(s_ml[j], s_o[j][d4], big_m, l, o, nan_seen);
     store4(a, (row0 + h) * kHd + 4 * d4, make_float4(o[0], o[1], o[2], o[3]),
            nan_seen ? __builtin_nanf("") : a.v_scale / l);
   }
@@ -1610,14 +1666,35 @@ __global__ __launch_bounds__(NW * 64) void decode_fast_kernel(DecodeArgs a) {
   Fast<QS, KS, GT, BS, NW>::run(a);
 }
 
+// Waves per SIMD the split is built for: three, except for the group-2
+// 16-bit instances, which need a few more registers than three allow
+template <typename KS, int GT>
+constexpr int split_waves_per_eu() {
+  return (GT == 2 && !std::is_same<KS, FP8S>::value) ? 2 : 3;
+}
 template <typename QS, typename KS, int GT, int BS>
-__global__ __launch_bounds__(kSplitWaves * 64) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kSplitWaves * 64) __attribute__((amdgpu_waves_per_eu(split_waves_per_eu<KS, GT>(), split_waves_per_eu<KS, GT>()))) void decode_split_kernel(DecodeArgs a) {
   Fast<QS, KS, GT, BS, kSplitWaves>::run_split(a);
 }
 
+// The fields the merge's first loads depend on come as separate scalar
+// arguments ahead of the struct, so that they arrive preloaded in SGPRs
+// instead of through dependent loads of the argument block.
 template <typename QS, typename KS, int GT, int BS>
-__global__ __launch_bounds__(64) void merge_parts_kernel(DecodeArgs a) {
-  Fast<QS, KS, GT, BS, kSplitWaves>::run_merge(a);
+__global__ __launch_bounds__(kMergeGroups * 32) void merge_parts_kernel(
+    const int32_t *ctx, const float *part_o, const float *part_m, int32_t max_parts, int32_t partition_size,
+    int32_t window, int32_t num_kv_heads, int32_t head_groups, int32_t group, int32_t max_blocks, DecodeArgs a) {
+  a.ctx = ctx;
+  a.part_o = const_cast<float *>(part_o);
+  a.part_m = const_cast<float *>(part_m);
+  a.max_parts = max_parts;
+  a.partition_size = partition_size;
+  a.window = window;
+  a.num_kv_heads = num_kv_heads;
+  a.head_groups = head_groups;
+  a.group = group;
+  a.max_blocks = max_blocks;
+  Fast<QS, KS, GT, BS, kSplitWaves>::run_merge(a, static_cast<int>(blockDim.x >> 5));
 }
 
 // workgroups of the fixed-partition split per compute unit (one wave each)
@@ -1689,12 +1766,19 @@ hipError_t launch_fast_bs(const DecodeArgs &a, hipStream_t s, const LaunchEvents
     const dim3 block(kSplitWaves * 64);
     const int64_t most = units * a.max_parts;
     const dim3 sgrid(static_cast<unsigned>(min(most, static_cast<int64_t>(device_compute_units()) * kSplitWgsPerCu)));
-    const dim3 mgrid(static_cast<unsigned>(units), static_cast<unsigned>((a.heads_per_wg + 1) / 2));
+    const dim3 mgrid(static_cast<unsigned>(units), static_cast<unsigned>(a.heads_per_wg));
+    // lane groups per merge workgroup: enough for one round of loads (8
+    // partitions a group) at the workspace's most partitions, at least 2
+    int ng = 2;
+    while (ng < kMergeGroups && 8 * ng < a.max_parts) ng *= 2;
+    const dim3 mblock(32 * ng);
     switch (a.heads_per_wg) {
 #define PA_SPLIT(G) \
       case G: \
         hipExtLaunchKernelGGL((decode_split_kernel<QS, KS, G, BS>), sgrid, block, 0, s, ev.start, nullptr, 0, a); \
-        hipExtLaunchKernelGGL((merge_parts_kernel<QS, KS, G, BS>), mgrid, dim3(64), 0, s, nullptr, ev.stop, 0, a); \
+        hipExtLaunchKernelGGL((merge_parts_kernel<QS, KS, G, BS>), mgrid, mblock, 0, s, nullptr, ev.stop, 0, a.ctx, \
+                              a.part_o, a.part_m, a.max_parts, a.partition_size, a.window, a.num_kv_heads, \
+                              a.head_groups, a.group, a.max_blocks, a); \
         break;
       PA_SPLIT(1) PA_SPLIT(2) PA_SPLIT(4) PA_SPLIT(8)
 #undef PA_SPLIT

@@ -71,15 +71,19 @@ __device__ __forceinline__ void swap16(uint32_t &a, uint32_t &b) {
 __device__ __forceinline__ void swap32(uint32_t &a, uint32_t &b) {
   asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
+// IEEE maximum (NaN-propagating), one v_max / v_maximum3 with no
+// canonicalising moves (fmaxf first quiets each operand it cannot prove
+// canonical, one extra instruction per operand)
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float xor16_max(float x) {
   uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
   swap16(a, b);
-  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  return max2(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 __device__ __forceinline__ float xor32_max(float x) {
   uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
   swap32(a, b);
-  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  return max2(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 __device__ __forceinline__ float xor16_sum(float x) {
   uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;

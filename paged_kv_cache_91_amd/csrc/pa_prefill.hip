@@ -56,9 +56,7 @@ constexpr int kRsrcWord3 = 0x00020000;     // buffer resource: raw buffer, 32-bi
 constexpr int kMfmaPrio = 1;              // wave priority during the matrix-core bursts (measured: 2 gains nothing)
 constexpr float kLazy = 8.0f;              // base-2 headroom before the running max moves
 
-// IEEE maximum (NaN-propagating): v_maximum3_f32 on gfx950, with none of the
-// quieting moves that fmaxf's operands get
-__device__ __forceinline__ float max2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+// max2 (pa_mfma.h): IEEE maximum, v_maximum3_f32 for two of them in a row
 __device__ __forceinline__ float max3(float a, float b, float c) { return max2(max2(a, b), c); }
 __device__ __forceinline__ float lanes16_max(float x) {        // over lanes l, l ^ 16, l ^ 32, l ^ 48
   uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
