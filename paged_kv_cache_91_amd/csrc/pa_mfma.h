@@ -35,6 +35,11 @@ template <> struct Mma<BF16S> {
   static __device__ __forceinline__ uint32_t pack2(float x, float y) {
     return __builtin_bit_cast(uint32_t, bf16x2_t{static_cast<__bf16>(x), static_cast<__bf16>(y)});
   }
+  // acc + the two bf16 values of a packed dword (a dot product with (1, 1))
+  static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, 0x3F803F80u),
+                                           acc, false);
+  }
   // two e4m3 codes (low or high half of w) -> two bf16 values, exact
   template <bool HI>
   static __device__ __forceinline__ uint32_t from_fp8(uint32_t w) {
@@ -52,6 +57,9 @@ template <> struct Mma<F16S> {
   }
   static __device__ __forceinline__ uint32_t pack2(float x, float y) {
     return __builtin_bit_cast(uint32_t, f16x2_t{static_cast<_Float16>(x), static_cast<_Float16>(y)});
+  }
+  static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), __builtin_bit_cast(f16x2_t, 0x3C003C00u), acc, false);
   }
   template <bool HI>
   static __device__ __forceinline__ uint32_t from_fp8(uint32_t w) {

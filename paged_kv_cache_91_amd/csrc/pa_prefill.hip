@@ -351,19 +351,22 @@ struct Prefill {
           }
         }
       }
-      float mz[kCg];
+      // Whether some column's maximum passes m_run + kLazy is decided on
+      // each lane's own 8 keys (m_run is the same in the four lanes of a
+      // column); the column maximum across lanes is only formed when it does.
+      float lmx[kCg];
       bool need = false;
 #pragma unroll
       for (int cg = 0; cg < kCg; ++cg) {
-        const float mx = lanes16_max(max3(max3(z[cg][0], z[cg][1], z[cg][2]), max3(z[cg][3], z[cg][4], z[cg][5]),
-                                          max2(z[cg][6], z[cg][7])));
-        mz[cg] = mx == -INFINITY ? -INFINITY : mx * sl;           // sl = 0 must not give NaN
-        need |= mz[cg] > m_run[cg] + kLazy;                       // true on a column's first keys
+        lmx[cg] = max3(max3(z[cg][0], z[cg][1], z[cg][2]), max3(z[cg][3], z[cg][4], z[cg][5]), max2(z[cg][6], z[cg][7]));
+        need |= lmx[cg] * sl > m_run[cg] + kLazy;                 // true on a column's first keys
       }
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
         for (int cg = 0; cg < kCg; ++cg) {
-          const float m_new = max2(m_run[cg], mz[cg]);
+          const float mx = lanes16_max(lmx[cg]);
+          const float mz = mx == -INFINITY ? -INFINITY : mx * sl;   // sl = 0 must not give NaN
+          const float m_new = max2(m_run[cg], mz);
           // a column that has seen no key keeps m = -inf; alpha is then 0
           const float alpha = __builtin_amdgcn_exp2f(m_run[cg] - (m_new == -INFINITY ? 0.0f : m_new));
           m_run[cg] = m_new;
@@ -384,9 +387,12 @@ struct Prefill {
 #pragma unroll
           for (int j = 0; j < 8; ++j) p[j] = z[cg][j] == -INFINITY ? 0.0f : p[j];
         }
-        l_run[cg] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        pb[cg] = __builtin_bit_cast(V8, make_uint4(M::pack2(p[0], p[1]), M::pack2(p[2], p[3]), M::pack2(p[4], p[5]),
-                                                   M::pack2(p[6], p[7])));
+        const uint4 pk = make_uint4(M::pack2(p[0], p[1]), M::pack2(p[2], p[3]), M::pack2(p[4], p[5]),
+                                    M::pack2(p[6], p[7]));
+        // the row sum takes the same rounded probabilities P.V multiplies
+        // (four two-term dot products with (1, 1))
+        l_run[cg] = M::sum2(pk.w, M::sum2(pk.z, M::sum2(pk.y, M::sum2(pk.x, l_run[cg]))));
+        pb[cg] = __builtin_bit_cast(V8, pk);
       }
       // O^T += V^T . P, MFMA e over head dims 16e .. 16e + 15: A holds, for
       // lane (m, g4), V of dim 16e + m at the lane's 8 key slots, which two
