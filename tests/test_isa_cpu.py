@@ -11,8 +11,9 @@ the signature of the intended schedule in decode_pair_kernel<bf16, bf16,
 group 4, block 16>, the kernel the Llama-3-8B-shaped layer runs:
 
 * the first waits inside the tile loop leave 14 loads outstanding;
-* at most a handful of vector dword loads in the whole kernel (set-up and
-  merge only).
+* no vector dword load inside the tile loop (the lengths and table entries
+  it reads are scalar loads), and only a few in the whole kernel (set-up and
+  merge).
 """
 
 import os
@@ -48,9 +49,28 @@ def test_tile_loop_keeps_two_tiles_in_flight(pair_isa):
     assert waits and max(waits[:3]) >= 12, waits[:8]
 
 
+def _loops_with_mfma(lines):
+    """(first, last) line of every loop (a backward branch) whose body holds an MFMA."""
+    labels = {m.group(1): i for i, l in enumerate(lines) for m in [re.match(r"^(\.LBB\w+):", l)] if m}
+    loops = []
+    for i, l in enumerate(lines):
+        m = re.search(r"s_c?branch\w*\s+(\.LBB\w+)", l)
+        if m and m.group(1) in labels and labels[m.group(1)] < i:
+            body = lines[labels[m.group(1)]:i + 1]
+            if any("v_mfma" in b for b in body):
+                loops.append((labels[m.group(1)], i))
+    return loops
+
+
 def test_tile_loop_reads_tables_and_lengths_with_scalar_loads(pair_isa):
+    lines = pair_isa.splitlines()
+    loops = _loops_with_mfma(lines)
+    assert loops
+    first, last = min(a for a, _ in loops), max(b for _, b in loops)
+    in_loop = [l for l in lines[first:last + 1] if re.search(r"\bglobal_load_dword\s", l)]
+    assert not in_loop, in_loop
     vector_dword_loads = len(re.findall(r"\bglobal_load_dword\s", pair_isa))
-    assert vector_dword_loads <= 8, vector_dword_loads
+    assert vector_dword_loads <= 16, vector_dword_loads
 
 
 # Prefill: the prefetched K/V chunks once went through scratch memory (an
