@@ -174,8 +174,10 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *                 0: single pass, one workgroup walks a whole context.
  *                 > 0: split-KV; a multiple of bs; partition p covers
  *                 positions [p*P, min((p+1)*P, n)); the partial results are
- *                 merged in increasing p, so the output does not depend on
- *                 the order in which partitions finish.
+ *                 merged in a fixed order (head dim 128: partitions j, j+g,
+ *                 j+2g, ... for each of g lane groups, then the groups in
+ *                 order; other shapes: increasing p), so the output does not
+ *                 depend on the order in which partitions finish.
  *   workspace     device scratch of at least pa_decode_workspace_bytes(...)
  *                 bytes when partition_size != 0 (else may be NULL).  Its
  *                 leading bytes hold counters, which MUST be zero before the
@@ -208,7 +210,7 @@ int pa_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
  * window - 1 before it.  Table entries of blocks wholly before lo
  * (j < lo / block_size) are never read, so they may name released blocks or
  * hold any value.  With partition_size > 0 the partitions are
- * [p*P, (p+1)*P) intersected with [lo, n), merged in increasing p.
+ * [p*P, (p+1)*P) intersected with [lo, n), merged in pa_decode's fixed order.
  *
  *   window    >= 0; 0 attends the whole context (pa_decode).
  * Every other argument, the workspace contract and the error behaviour are
