@@ -121,6 +121,24 @@ def test_decode_shapes(shape):
     check_decode(wl, parts=(0, bs, 4 * bs, 512 if 512 % bs == 0 else 8 * bs, pa.PA_PARTITION_AUTO))
 
 
+@pytest.mark.parametrize("shape", [("bf16", "bf16", 32, 8, 128, 16), ("f16", "f16", 8, 8, 128, 16),
+                                   ("bf16", "bf16", 64, 8, 128, 32)], ids=lambda s: "-".join(map(str, s)))
+def test_fixed_split_merges_many_partitions(shape):
+    """The fixed split's merge folds a sequence's partitions in rounds of 8
+    per lane group (up to 8 groups): with one block per partition, lengths
+    of 16 to 3030 positions give from 1 to ~190 partitions, covering one and
+    several rounds, groups with no partition, and a last round only partly
+    filled."""
+    qd, kd, hq, hkv, d, bs = shape
+    rng = np.random.default_rng(700 + hq + bs)
+    lens = np.array([16, 17, 1024, 1025, 2049, 3030])
+    need = sum(-(-int(n) // bs) for n in lens)
+    wl = W.build_decode(700 + hq, name=f"many-parts-{qd}", q_dtype=qd, kv_dtype=kd, num_q_heads=hq,
+                        num_kv_heads=hkv, head_dim=d, block_size=bs, num_blocks=need + 3,
+                        context_lens=lens, rng=rng)
+    check_decode(wl, parts=(bs, 16 * bs, pa.PA_PARTITION_AUTO), label="many partitions")
+
+
 FP8_SHAPES = [
     ("bf16", "bf16", 64, 8, 128, 32),     # long-context fp8 layer shape
     ("bf16", "f32", 8, 2, 64, 16),
