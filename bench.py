@@ -330,8 +330,10 @@ def cpu_baseline(wl, new_k, new_v, nseq, min_seconds=10.0, max_passes=50):
 
 
 def other_workload(args, pa, W, torch, dev):
-    """pa_decode alone on one of the other batches, timed with HIP events per
-    call (after its cache write or block copies, which are not timed).  Their
+    """pa_decode alone on one of the other batches, timed per call (after its
+    cache write or block copies, which are not timed) by the event pair the
+    launch records around its kernels, and again by events on the stream
+    around the call, which also hold the launch gaps.  Their
     pools are 1-21 GB, past the 256 MB last-level cache, except the prefix
     batch's (about 40 MB of distinct blocks): its numbers are cache-warm."""
     import numpy as np
@@ -398,6 +400,20 @@ def other_workload(args, pa, W, torch, dev):
         for _ in range(max(args.warmup, 3)):
             call()
         steps = max(1, min(args.steps, 50))
+        # the decode kernels alone: the event pair the call's launch records
+        # as its first kernel begins and its last ends (as the main bench's
+        # roofline); then, for reference, events on the stream around each call
+        kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in kev:
+            a.record(stream)               # creates the events
+            b.record(stream)
+        torch.cuda.synchronize()
+        for a, b in kev:
+            pa.pa_time_next_decode(a, b)
+            call()
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in kev)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
         torch.cuda.synchronize()
@@ -406,7 +422,7 @@ def other_workload(args, pa, W, torch, dev):
             call()
             b.record(stream)
         torch.cuda.synchronize()
-        us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+        call_us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
         med = us[len(us) // 2]
         gbs = kv_bytes / (med * 1e-6) / 1e9
         assert bool(torch.isfinite(out.float()).all()), "non-finite output"
@@ -415,7 +431,11 @@ def other_workload(args, pa, W, torch, dev):
             "kv_dtype": wl.kv_dtype, "num_seqs": wl.num_seqs, "num_q_heads": wl.num_q_heads,
             "num_kv_heads": wl.num_kv_heads, "block_size": wl.block_size,
             "decode_us": {"median": round(med, 2), "p10": round(us[len(us) // 10], 2),
-                          "p90": round(us[(9 * len(us)) // 10], 2), "calls": steps},
+                          "p90": round(us[(9 * len(us)) // 10], 2), "calls": steps,
+                          "timing": "events the launch records as its kernels begin and end"},
+            "call_us": {"median": round(call_us[len(call_us) // 2], 2), "p10": round(call_us[len(call_us) // 10], 2),
+                        "p90": round(call_us[(9 * len(call_us)) // 10], 2),
+                        "timing": "events on the stream around the whole call"},
             "kv_gbs": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "decode_tokens_per_s_per_layer": round(wl.num_seqs / (med * 1e-6), 1),
             "cache": "warm (fits the last-level cache)" if kv_bytes < (256 << 20) else "pools exceed the last-level cache",
