@@ -21,11 +21,14 @@ Reported (one JSON line):
                context_len positions x 8 heads x 128 x 2 bytes x K and V) over
                the synchronised wall time of the timed steps;
   roofline     the decode kernel alone, timed with the HIP event pair its
-               launch records as it begins and ends (pa_time_next_decode):
+               launch records as it begins and ends (pa_time_next_decode),
+               events created for timing only (hipEventDisableSystemFence:
+               recording one performs no system-scope release, the cache
+               write-back a default event adds to the interval):
                algorithmic bytes per launch / MEDIAN event duration, against
-               MI355X's 8 TB/s HBM peak (the mean is reported beside it;
-               stream_bracket_mean_us: events recorded on the stream around
-               the whole call, for reference).  `traffic` is the HBM byte
+               MI355X's 8 TB/s HBM peak (beside it: the mean; the same pair
+               as default events, fence included; stream_bracket_mean_us,
+               default events on the stream around the whole call).  `traffic` is the HBM byte
                count per launch from the committed rocprofv3 counter runs
                (profiles/decode_traffic.json: the L2-to-memory read and write
                requests counted by size), reported only while the decode
@@ -84,6 +87,69 @@ def log(msg):
 
 
 DECODE_SOURCES = ("pa_decode_fast.hip", "pa_common.h", "pa_internal.h", "pa_mfma.h")
+
+
+class TimingEvent:
+    """A HIP event created for timing only (hipEventDisableSystemFence), in
+    the HIP runtime torch has loaded.  A default event performs a
+    system-scope release when it is recorded, which writes back and
+    invalidates caches inside the measured interval; this one does not.
+    Same surface as the torch.cuda.Event calls used here."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        if TimingEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so.7")      # the runtime already loaded (by soname)
+            hip.hipGetErrorString.restype = ctypes.c_char_p
+            TimingEvent._hip = hip
+        h = ctypes.c_void_p()
+        self._check(TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(h),
+                                                             ctypes.c_uint(self.DISABLE_SYSTEM_FENCE)))
+        self.cuda_event = h.value
+
+    @staticmethod
+    def _check(rc):
+        if rc != 0:
+            raise RuntimeError(f"HIP event call failed: {TimingEvent._hip.hipGetErrorString(rc).decode()}")
+
+    def record(self, stream):
+        import ctypes
+        self._check(TimingEvent._hip.hipEventRecord(ctypes.c_void_p(self.cuda_event),
+                                                    ctypes.c_void_p(stream.cuda_stream)))
+
+    def elapsed_time(self, end):
+        import ctypes
+        ms = ctypes.c_float()
+        self._check(TimingEvent._hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.cuda_event),
+                                                         ctypes.c_void_p(end.cuda_event)))
+        return ms.value
+
+    def __del__(self):
+        if getattr(self, "cuda_event", None) and TimingEvent._hip is not None:
+            import ctypes
+            TimingEvent._hip.hipEventDestroy(ctypes.c_void_p(self.cuda_event))
+            self.cuda_event = None
+
+
+def kernel_timed(torch, stream, steps, run, timing_only=True):
+    """Durations (ms) of ``steps`` calls of ``run(i, (start, stop))``, each
+    handing the event pair to the call's launch (pa_time_next_decode), so
+    that the pair is recorded as its first kernel begins and its last ends."""
+    if timing_only:
+        pairs = [(TimingEvent(), TimingEvent()) for _ in range(steps)]
+    else:
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(steps)]
+    for a, b in pairs:
+        a.record(stream)               # both kinds exist once recorded
+        b.record(stream)
+    torch.cuda.synchronize()
+    for i, ev in enumerate(pairs):
+        run(i, ev)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in pairs]
 
 
 def recorded_traffic(partition):
@@ -214,19 +280,12 @@ def main():
     log(f"[bench] timed {args.steps} steps in {elapsed:.4f}s")
 
     # timed region 2 (the roofline): K more steps, the decode kernel recording
-    # its own event pair as it begins and ends.  Those events cost the stream
-    # a few microseconds per call, so they stay out of region 1.
-    kernel_events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                     for _ in range(args.steps)]
-    for a, b in kernel_events:
-        a.record(stream)               # creates the events
-        b.record(stream)
-    torch.cuda.synchronize()
-    for k in range(args.steps):
-        step(k, kernel_ev=kernel_events[k])
-    torch.cuda.synchronize()
-    decode_ms = [a.elapsed_time(b) for a, b in kernel_events]
-    log(f"[bench] timed {args.steps} more steps with kernel events")
+    # its own event pair as it begins and ends (timing-only events), then K
+    # with default events for comparison.  Those events cost the stream a
+    # few microseconds per call, so they stay out of region 1.
+    decode_ms = kernel_timed(torch, stream, args.steps, lambda k, ev: step(k, kernel_ev=ev))
+    fenced_ms = kernel_timed(torch, stream, args.steps, lambda k, ev: step(k, kernel_ev=ev), timing_only=False)
+    log(f"[bench] timed 2 x {args.steps} more steps with kernel events")
 
     kv_bytes = wl.kv_bytes()
     ms_per_step = elapsed * 1e3 / args.steps
@@ -270,13 +329,14 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "traffic_source": traffic_src,
-            "timing": "HIP events recorded by the decode kernel's launch as it begins and ends; "
-                      "achieved uses the median",
+            "timing": "HIP events recorded by the decode kernel's launch as it begins and ends, created "
+                      "for timing only (hipEventDisableSystemFence); achieved uses the median",
             "achieved_at_mean": round(kv_bytes / (dec_mean * 1e-3) / 1e9, 2),
             "mean_us": round(dec_mean * 1e3, 2),
             "median_us": round(dec_med * 1e3, 2),
             "p10_us": round(sorted(decode_ms)[len(decode_ms) // 10] * 1e3, 2),
             "p90_us": round(sorted(decode_ms)[(9 * len(decode_ms)) // 10] * 1e3, 2),
+            "default_events_median_us": round(statistics.median(fenced_ms) * 1e3, 2),
             "stream_bracket_mean_us": round(statistics.fmean(bracket_ms) * 1e3, 2),
         },
         "cpu_baseline": None,
@@ -403,17 +463,10 @@ def other_workload(args, pa, W, torch, dev):
         # the decode kernels alone: the event pair the call's launch records
         # as its first kernel begins and its last ends (as the main bench's
         # roofline); then, for reference, events on the stream around each call
-        kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
-        for a, b in kev:
-            a.record(stream)               # creates the events
-            b.record(stream)
-        torch.cuda.synchronize()
-        for a, b in kev:
-            pa.pa_time_next_decode(a, b)
+        def timed_call(i, ev):
+            pa.pa_time_next_decode(ev[0], ev[1])
             call()
-        torch.cuda.synchronize()
-        us = sorted(a.elapsed_time(b) * 1e3 for a, b in kev)
+        us = sorted(x * 1e3 for x in kernel_timed(torch, stream, steps, timed_call))
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
         torch.cuda.synchronize()
@@ -432,10 +485,10 @@ def other_workload(args, pa, W, torch, dev):
             "num_kv_heads": wl.num_kv_heads, "block_size": wl.block_size,
             "decode_us": {"median": round(med, 2), "p10": round(us[len(us) // 10], 2),
                           "p90": round(us[(9 * len(us)) // 10], 2), "calls": steps,
-                          "timing": "events the launch records as its kernels begin and end"},
+                          "timing": "timing-only events the launch records as its kernels begin and end"},
             "call_us": {"median": round(call_us[len(call_us) // 2], 2), "p10": round(call_us[len(call_us) // 10], 2),
                         "p90": round(call_us[(9 * len(call_us)) // 10], 2),
-                        "timing": "events on the stream around the whole call"},
+                        "timing": "default events on the stream around the whole call"},
             "kv_gbs": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "decode_tokens_per_s_per_layer": round(wl.num_seqs / (med * 1e-6), 1),
             "cache": "warm (fits the last-level cache)" if kv_bytes < (256 << 20) else "pools exceed the last-level cache",

@@ -328,9 +328,10 @@ def pa_swap_blocks(src: KvPool, dst: KvPool, src_dst_pairs: torch.Tensor, stream
 
 
 def pa_time_next_decode(start, stop) -> None:
-    """Have the next pa_decode on this thread record ``start`` / ``stop``
-    (timing-enabled torch.cuda.Event objects, already recorded once so that
-    they exist) as its kernels begin and end."""
+    """Have the next pa_decode on this thread record ``start`` / ``stop`` as
+    its kernels begin and end.  Each is an object whose ``cuda_event`` is a
+    timing-enabled HIP event handle that exists (a torch.cuda.Event exists
+    once it has been recorded)."""
     if (start is None) != (stop is None):
         raise ValueError("give both events or neither")
     _check(lib().pa_time_next_decode(None if start is None else start.cuda_event,
