@@ -122,7 +122,9 @@ int pa_write_kv(const void *k, const void *v, int32_t src_dtype, int32_t num_tok
  * pa_decode_workspace_bytes -- device scratch pa_decode needs in split mode:
  * one 64-bit arrival counter per (sequence, group of up to 8 query heads
  * sharing a KV head), padded to 256 bytes, then float32 partial maxima, sums
- * and outputs.  With partition_size > 0 there is a partial for every
+ * and outputs (head dim 128 with partition_size > 0 stores each partial
+ * output normalised by its sum and rounded to the query dtype, in the same
+ * space).  With partition_size > 0 there is a partial for every
  * (sequence, query head slot, partition), with
  * ceil(max_blocks_per_seq * block_size / partition_size) partitions per
  * sequence.  With PA_PARTITION_AUTO there are two partials per streaming wave the

@@ -500,6 +500,16 @@ struct Fast {
     }
     return w;
   }
+  // pack4's inverse: four values of the q dtype (two dwords) as floats
+  static __device__ __forceinline__ f32x4_t unpack4(uint2 w) {
+    if constexpr (std::is_same<QS, BF16S>::value) {
+      return f32x4_t{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+    } else {
+      const auto h = [](uint32_t b) { return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b))); };
+      return f32x4_t{h(w.x & 0xffffu), h(w.x >> 16), h(w.y & 0xffffu), h(w.y >> 16)};
+    }
+  }
   // four consecutive outputs, scaled by mul and rounded to the q dtype
   static __device__ __forceinline__ void store4(const DecodeArgs &a, int64_t idx, float4 o, float mul) {
     *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + idx) =
@@ -1579,17 +1589,20 @@ struct Fast {
     }
 
     // split: publish this partition's partial; the merge is a launch of its
-    // own (run_merge), which sees it once this launch has ended
+    // own (run_merge), which sees it once this launch has ended.  The
+    // partial output is stored normalised (o / l, a weighted mean of V rows,
+    // so within the range of the cache's values) and rounded to the q dtype,
+    // half the bytes of float32; m and l stay float32.
     const int64_t unit = static_cast<int64_t>(seq) * (a.num_kv_heads * a.head_groups) + y;
-    float *po = a.part_o + (unit * a.max_parts + part) * (GT * kHd);
+    uint16_t *po = reinterpret_cast<uint16_t *>(a.part_o) + (unit * a.max_parts + part) * (GT * kHd);
     float *pml = a.part_m + (unit * a.max_parts + part) * (GT * 2);
     for (int i = tid; i < GT * (kHd / 4); i += kThreads) {
       const int h = i >> 5, d4 = i & 31;
       float big_m, l;
       float4 o;
       wave_merge(h, d4, big_m, l, o);
-      const float mul = any_bad ? nanv : 1.0f;
-      *reinterpret_cast<float4 *>(po + h * kHd + 4 * d4) = make_float4(o.x * mul, o.y * mul, o.z * mul, o.w * mul);
+      const float mul = any_bad ? nanv : 1.0f / l;     // l >= 1: the running max's own term
+      *reinterpret_cast<uint2 *>(po + h * kHd + 4 * d4) = pack4(make_float4(o.x * mul, o.y * mul, o.z * mul, o.w * mul));
       if (d4 == 0) *reinterpret_cast<float2 *>(pml + 2 * h) = make_float2(any_bad ? nanv : big_m, any_bad ? nanv : l);
     }
   }
@@ -1622,22 +1635,23 @@ struct Fast {
     const int g = static_cast<int>(threadIdx.x >> 5);
     const int d4 = threadIdx.x & 31;
     const int64_t row0 = static_cast<int64_t>(seq) * a.num_q_heads + kvh * a.group + hg * GT;
-    const float *bo = a.part_o + unit * a.max_parts * (GT * kHd) + h * kHd + 4 * d4;
+    const uint16_t *bo = reinterpret_cast<const uint16_t *>(a.part_o) + unit * a.max_parts * (GT * kHd) + h * kHd + 4 * d4;
     const float *bml = a.part_m + unit * a.max_parts * (GT * 2) + 2 * h;
     float big_m = -INFINITY, l = 0.0f, o[4] = {0, 0, 0, 0};
     bool nan_seen = false;
     for (int p0 = g; p0 < nparts; p0 += 8 * ng) {
       f32x2_t ml[8];
-      f32x4_t ov[8];
+      uint2 ov[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int pp = min(p0 + k * ng, nparts - 1);
         ml[k] = *reinterpret_cast<const f32x2_t *>(bml + pp * GT * 2);
-        ov[k] = *reinterpret_cast<const f32x4_t *>(bo + pp * GT * kHd);
+        ov[k] = *reinterpret_cast<const uint2 *>(bo + pp * GT * kHd);
       }
+      // a partial's unnormalised output is its stored mean times its l
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        if (p0 + k * ng < nparts) fold4(ml[k], ov[k], big_m, l, o, nan_seen);
+        if (p0 + k * ng < nparts) fold4(ml[k], unpack4(ov[k]) * ml[k][1], big_m, l, o, nan_seen);
     }
     // groups 0 .. min(ng, nparts) - 1 hold at least one partition each
     s_o[g][d4] = f32x4_t{o[0], o[1], o[2], o[3]};
