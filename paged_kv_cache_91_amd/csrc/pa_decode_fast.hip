@@ -1618,10 +1618,31 @@ struct Fast {
   static __device__ void run_merge(const DecodeArgs &a, int ng) {
     __shared__ f32x4_t s_o[kMergeGroups][32];
     __shared__ f32x2_t s_ml[kMergeGroups];
-    const int64_t unit = blockIdx.x;
+    const int unit = static_cast<int>(blockIdx.x);
+    const int h = static_cast<int>(blockIdx.y);
+    const int g = static_cast<int>(threadIdx.x >> 5);
+    const int d4 = threadIdx.x & 31;
+    const uint16_t *bo = reinterpret_cast<const uint16_t *>(a.part_o) +
+                         static_cast<int64_t>(unit) * a.max_parts * (GT * kHd) + h * kHd + 4 * d4;
+    const float *bml = a.part_m + static_cast<int64_t>(unit) * a.max_parts * (GT * 2) + 2 * h;
+    f32x2_t ml[8];
+    uint2 ov[8];
+    auto load_round = [&](int p0, int last) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int pp = min(p0 + k * ng, last);
+        ml[k] = *reinterpret_cast<const f32x2_t *>(bml + pp * GT * 2);
+        ov[k] = *reinterpret_cast<const uint2 *>(bo + pp * GT * kHd);
+      }
+    };
+    // The first round's loads go out before the sequence's length arrives:
+    // every slot below max_parts lies inside the workspace, and slots past
+    // the sequence's partitions are loaded but never folded.
+    load_round(g, a.max_parts - 1);
+    asm volatile("" ::: "memory");     // keep those loads ahead of the length's
     const int KVG = a.num_kv_heads * a.head_groups;
-    const int seq = static_cast<int>(unit / KVG);
-    const int y = static_cast<int>(unit - static_cast<int64_t>(seq) * KVG);
+    const int seq = unit / KVG;
+    const int y = unit - seq * KVG;
     const int kvh = y / a.head_groups;
     const int hg = y - kvh * a.head_groups;
     const int n = load_const(a.ctx, seq);
@@ -1629,25 +1650,13 @@ struct Fast {
     const int P = a.partition_size;
     const int nparts = (n + P - 1) / P - window_lo(n, a.window) / P;
     if (nparts <= 1) return;
-    const int h = static_cast<int>(blockIdx.y);
     const int hcount = min(GT, a.group - hg * GT);
     if (h >= hcount) return;
-    const int g = static_cast<int>(threadIdx.x >> 5);
-    const int d4 = threadIdx.x & 31;
     const int64_t row0 = static_cast<int64_t>(seq) * a.num_q_heads + kvh * a.group + hg * GT;
-    const uint16_t *bo = reinterpret_cast<const uint16_t *>(a.part_o) + unit * a.max_parts * (GT * kHd) + h * kHd + 4 * d4;
-    const float *bml = a.part_m + unit * a.max_parts * (GT * 2) + 2 * h;
     float big_m = -INFINITY, l = 0.0f, o[4] = {0, 0, 0, 0};
     bool nan_seen = false;
     for (int p0 = g; p0 < nparts; p0 += 8 * ng) {
-      f32x2_t ml[8];
-      uint2 ov[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int pp = min(p0 + k * ng, nparts - 1);
-        ml[k] = *reinterpret_cast<const f32x2_t *>(bml + pp * GT * 2);
-        ov[k] = *reinterpret_cast<const uint2 *>(bo + pp * GT * kHd);
-      }
+      if (p0 != g) load_round(p0, nparts - 1);
       // a partial's unnormalised output is its stored mean times its l
 #pragma unroll
       for (int k = 0; k < 8; ++k)
@@ -1696,8 +1705,9 @@ __global__ __launch_bounds__(kSplitWaves * 64) __attribute__((amdgpu_waves_per_e
 // instead of through dependent loads of the argument block.
 template <typename QS, typename KS, int GT, int BS>
 __global__ __launch_bounds__(kMergeGroups * 32) void merge_parts_kernel(
-    const int32_t *ctx, const float *part_o, const float *part_m, int32_t max_parts, int32_t partition_size,
-    int32_t window, int32_t num_kv_heads, int32_t head_groups, int32_t group, int32_t max_blocks, DecodeArgs a) {
+    const int32_t *ctx, const float *part_o, const float *part_m, int32_t ng, int32_t max_parts,
+    int32_t partition_size, int32_t window, int32_t num_kv_heads, int32_t head_groups, int32_t group,
+    int32_t max_blocks, DecodeArgs a) {
   a.ctx = ctx;
   a.part_o = const_cast<float *>(part_o);
   a.part_m = const_cast<float *>(part_m);
@@ -1708,7 +1718,7 @@ __global__ __launch_bounds__(kMergeGroups * 32) void merge_parts_kernel(
   a.head_groups = head_groups;
   a.group = group;
   a.max_blocks = max_blocks;
-  Fast<QS, KS, GT, BS, kSplitWaves>::run_merge(a, static_cast<int>(blockDim.x >> 5));
+  Fast<QS, KS, GT, BS, kSplitWaves>::run_merge(a, ng);     // ng lane groups: blockDim.x / 32
 }
 
 // workgroups of the fixed-partition split per compute unit (one wave each)
@@ -1791,7 +1801,7 @@ hipError_t launch_fast_bs(const DecodeArgs &a, hipStream_t s, const LaunchEvents
       case G: \
         hipExtLaunchKernelGGL((decode_split_kernel<QS, KS, G, BS>), sgrid, block, 0, s, ev.start, nullptr, 0, a); \
         hipExtLaunchKernelGGL((merge_parts_kernel<QS, KS, G, BS>), mgrid, mblock, 0, s, nullptr, ev.stop, 0, a.ctx, \
-                              a.part_o, a.part_m, a.max_parts, a.partition_size, a.window, a.num_kv_heads, \
+                              a.part_o, a.part_m, ng, a.max_parts, a.partition_size, a.window, a.num_kv_heads, \
                               a.head_groups, a.group, a.max_blocks, a); \
         break;
       PA_SPLIT(1) PA_SPLIT(2) PA_SPLIT(4) PA_SPLIT(8)
