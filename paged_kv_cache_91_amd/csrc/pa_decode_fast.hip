@@ -75,6 +75,9 @@ __device__ __forceinline__ void coherent_store(float *p, float x) {
 __device__ __forceinline__ void coherent_store4(float *p, f32x4_t v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
 }
+__device__ __forceinline__ void coherent_store2(void *p, uint2 v) {
+  asm volatile("global_store_dwordx2 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
 __device__ __forceinline__ f32x4_t coherent_load4(const float *p) {
   f32x4_t r;
   asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=&v"(r) : "v"(p) : "memory");
@@ -1592,7 +1595,9 @@ struct Fast {
     // own (run_merge), which sees it once this launch has ended.  The
     // partial output is stored normalised (o / l, a weighted mean of V rows,
     // so within the range of the cache's values) and rounded to the q dtype,
-    // half the bytes of float32; m and l stay float32.
+    // half the bytes of float32; m and l stay float32.  The stores write
+    // through to the device-coherent level, so that the launch does not end
+    // with the partials as dirty lines in every L2 to write back.
     const int64_t unit = static_cast<int64_t>(seq) * (a.num_kv_heads * a.head_groups) + y;
     uint16_t *po = reinterpret_cast<uint16_t *>(a.part_o) + (unit * a.max_parts + part) * (GT * kHd);
     float *pml = a.part_m + (unit * a.max_parts + part) * (GT * 2);
@@ -1602,8 +1607,9 @@ struct Fast {
       float4 o;
       wave_merge(h, d4, big_m, l, o);
       const float mul = any_bad ? nanv : 1.0f / l;     // l >= 1: the running max's own term
-      *reinterpret_cast<uint2 *>(po + h * kHd + 4 * d4) = pack4(make_float4(o.x * mul, o.y * mul, o.z * mul, o.w * mul));
-      if (d4 == 0) *reinterpret_cast<float2 *>(pml + 2 * h) = make_float2(any_bad ? nanv : big_m, any_bad ? nanv : l);
+      coherent_store2(po + h * kHd + 4 * d4, pack4(make_float4(o.x * mul, o.y * mul, o.z * mul, o.w * mul)));
+      if (d4 == 0)
+        coherent_store2(pml + 2 * h, __builtin_bit_cast(uint2, make_float2(any_bad ? nanv : big_m, any_bad ? nanv : l)));
     }
   }
 
@@ -1721,8 +1727,12 @@ __global__ __launch_bounds__(kMergeGroups * 32) void merge_parts_kernel(
   Fast<QS, KS, GT, BS, kSplitWaves>::run_merge(a, ng);     // ng lane groups: blockDim.x / 32
 }
 
-// workgroups of the fixed-partition split per compute unit (one wave each)
-constexpr int kSplitWgsPerCu = 32;
+// Most workgroups of the fixed-partition split per compute unit (one wave
+// each; the grid is also capped by the workspace's partitions per sequence).
+// Measured: 128 beats 32 and 64 (fewer items per workgroup, so the
+// dispatcher balances the tail) and 256 (a grid mostly past the batch's
+// items, whose workgroups only scan the lengths and leave).
+constexpr int kSplitWgsPerCu = 128;
 
 template <typename QS, typename KS, int GT, int BS, bool WIN>
 // The fields the launch's first loads depend on come as separate scalar
