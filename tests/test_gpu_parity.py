@@ -139,11 +139,49 @@ def test_fixed_split_merges_many_partitions(shape):
     check_decode(wl, parts=(bs, 16 * bs, pa.PA_PARTITION_AUTO), label="many partitions")
 
 
+@pytest.mark.parametrize("kv", ["f16", "bf16"])
+def test_split_partials_hold_large_values(kv):
+    """The fixed split keeps each partition's output as a mean of V rows in
+    the query dtype.  With every V value made positive and multiplied by
+    2^12 (both exact; f16 values then reach ~2e4), the outputs are exactly
+    2^12 times those of the positive unscaled problem, so out / 2^12 must
+    meet the usual bar against the oracle on that problem at every partition
+    size.  A partial kept unnormalised (a weighted sum of up to P rows)
+    would pass f16's largest finite value here."""
+    rng = np.random.default_rng(880)
+    lens = np.array([1, 16, 17, 255, 256, 1000, 2049])
+    bs = 16
+    need = sum(-(-int(n) // bs) for n in lens)
+    wl = W.build_decode(880, name=f"large-v-{kv}", q_dtype=kv, kv_dtype=kv, num_q_heads=32,
+                        num_kv_heads=8, head_dim=128, block_size=bs, num_blocks=need + 3,
+                        context_lens=lens, rng=rng)
+    mul = 4096.0
+    if kv == "bf16":
+        wl.v_pool = wl.v_pool & np.uint16(0x7FFF)
+        ref = oracle_out(wl)
+        widened = (wl.v_pool.astype(np.uint32) << 16).view(np.float32) * np.float32(mul)
+        wl.v_pool = (widened.view(np.uint32) >> 16).astype(np.uint16)
+    else:
+        wl.v_pool = np.abs(wl.v_pool)
+        ref = oracle_out(wl)
+        wl.v_pool = wl.v_pool * np.float16(mul)
+        assert np.isfinite(wl.v_pool).all()
+    dev = DeviceWorkload(wl)
+    for p in (0, bs, 4 * bs, 512, pa.PA_PARTITION_AUTO):
+        got = out_f64(dev.decode(partition_size=p))
+        assert np.isfinite(got).all(), f"partition {p}"
+        err = max_err(got / mul, ref)
+        say(f"    large V ({kv}) partition {p}: max abs err of out / 2^12 {err:.3e}")
+        assert err <= tol_for(wl), f"partition {p}: {err}"
+
+
 FP8_SHAPES = [
     ("bf16", "bf16", 64, 8, 128, 32),     # long-context fp8 layer shape
     ("bf16", "f32", 8, 2, 64, 16),
     ("f16", "f16", 4, 4, 128, 8),
     ("bf16", "bf16", 16, 2, 256, 16),
+    ("f16", "f16", 16, 4, 128, 32),       # f16 queries on the matrix-core kernels, group 4
+    ("f16", "f16", 8, 8, 128, 16),        # the same, one head per KV head
 ]
 
 
