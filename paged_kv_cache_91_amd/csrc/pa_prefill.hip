@@ -272,17 +272,20 @@ struct Prefill {
     // scratch-memory lookup)
     auto stage = [&](int buf, int t) {
       const int kbase = uniform((kt0 + t) * kKeys);
-      uint4 v0 = sv0, v1 = sv1;
-      if (kbase < klo || kbase + kKeys > khi) {
-        const uint32_t m0 = (kbase + rr >= klo && kbase + rr < khi) ? ~0u : 0u;
-        const uint32_t m1 = (kbase + rr + 16 >= klo && kbase + rr + 16 < khi) ? ~0u : 0u;
-        v0 = make_uint4(v0.x & m0, v0.y & m0, v0.z & m0, v0.w & m0);
-        v1 = make_uint4(v1.x & m1, v1.y & m1, v1.z & m1, v1.w & m1);
-      }
+      uint4 *v0 = reinterpret_cast<uint4 *>(&s_v[buf][rr * kRowBytes + ch * 16]);
+      uint4 *v1 = reinterpret_cast<uint4 *>(&s_v[buf][(rr + 16) * kRowBytes + ch * 16]);
       *reinterpret_cast<uint4 *>(&s_k[buf][rr * kRowBytes + ch * 16]) = sk0;
-      *reinterpret_cast<uint4 *>(&s_v[buf][rr * kRowBytes + ch * 16]) = v0;
+      *v0 = sv0;
       *reinterpret_cast<uint4 *>(&s_k[buf][(rr + 16) * kRowBytes + ch * 16]) = sk1;
-      *reinterpret_cast<uint4 *>(&s_v[buf][(rr + 16) * kRowBytes + ch * 16]) = v1;
+      *v1 = sv1;
+      // rows outside the range are then overwritten with zeros by the thread
+      // that staged them (its LDS writes land in order), which keeps the
+      // fetched registers flowing straight into the stores above
+      if (kbase < klo || kbase + kKeys > khi) {
+        const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+        if (!(kbase + rr >= klo && kbase + rr < khi)) *v0 = zero;
+        if (!(kbase + rr + 16 >= klo && kbase + rr + 16 < khi)) *v1 = zero;
+      }
     };
 
     // Transposing read (ds_read_b64_tr_b16): within each 16-lane block, lane
