@@ -19,7 +19,8 @@ K/V reads come from HBM rather than from the 256 MB last-level cache.
 Reported (one JSON line):
   value        KV-read GB/s of the whole step: algorithmic K/V bytes (exactly
                context_len positions x 8 heads x 128 x 2 bytes x K and V) over
-               the synchronised wall time of the timed steps;
+               the synchronised wall time of the timed steps, enqueued back to
+               back with nothing recorded between them;
   roofline     the decode kernel alone, timed with the HIP event pair its
                launch records as it begins and ends (pa_time_next_decode),
                events created for timing only (hipEventDisableSystemFence:
@@ -266,26 +267,32 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup {warmup_run} steps done")
 
-    # timed region 1 (the value): K steps, each decode call bracketed by a
-    # pair of events on the stream
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    # timed region 1 (the value): K steps as they are, nothing recorded
+    # between them
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
-        step(k, ev=events[k])
+        step(k)
+    enqueued = time.perf_counter() - t_start        # host time to issue the steps
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    bracket_ms = [a.elapsed_time(b) for a, b in events]
     log(f"[bench] timed {args.steps} steps in {elapsed:.4f}s")
 
     # timed region 2 (the roofline): K more steps, the decode kernel recording
     # its own event pair as it begins and ends (timing-only events), then K
-    # with default events for comparison.  Those events cost the stream a
-    # few microseconds per call, so they stay out of region 1.
+    # with default events for comparison.  Events cost the stream a few
+    # microseconds per call, so none are recorded in region 1.
     decode_ms = kernel_timed(torch, stream, args.steps, lambda k, ev: step(k, kernel_ev=ev))
     fenced_ms = kernel_timed(torch, stream, args.steps, lambda k, ev: step(k, kernel_ev=ev), timing_only=False)
     log(f"[bench] timed 2 x {args.steps} more steps with kernel events")
+    # for reference: default events on the stream around each decode call
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        step(k, ev=events[k])
+    torch.cuda.synchronize()
+    bracket_ms = [a.elapsed_time(b) for a, b in events]
 
     kv_bytes = wl.kv_bytes()
     ms_per_step = elapsed * 1e3 / args.steps
@@ -304,6 +311,7 @@ def main():
         "warmup": args.warmup,
         "warmup_steps_run": warmup_run,
         "ms_per_step": round(ms_per_step, 5),
+        "host_enqueue_ms_per_step": round(enqueued * 1e3 / args.steps, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
