@@ -75,8 +75,10 @@ __device__ __forceinline__ void coherent_store(float *p, float x) {
 __device__ __forceinline__ void coherent_store4(float *p, f32x4_t v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
 }
-__device__ __forceinline__ void coherent_store2(void *p, uint2 v) {
-  asm volatile("global_store_dwordx2 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+// the same 8-byte store at a uniform base (SGPRs) plus a per-lane byte
+// offset: one offset register per lane instead of a 64-bit address
+__device__ __forceinline__ void coherent_store2_at(const void *base, uint32_t off, uint2 v) {
+  asm volatile("global_store_dwordx2 %0, %1, %2 sc1" : : "v"(off), "v"(v), "s"(base) : "memory");
 }
 __device__ __forceinline__ f32x4_t coherent_load4(const float *p) {
   f32x4_t r;
@@ -1607,9 +1609,9 @@ struct Fast {
       float4 o;
       wave_merge(h, d4, big_m, l, o);
       const float mul = any_bad ? nanv : 1.0f / l;     // l >= 1: the running max's own term
-      coherent_store2(po + h * kHd + 4 * d4, pack4(make_float4(o.x * mul, o.y * mul, o.z * mul, o.w * mul)));
+      coherent_store2_at(po, (h * kHd + 4 * d4) * 2, pack4(make_float4(o.x * mul, o.y * mul, o.z * mul, o.w * mul)));
       if (d4 == 0)
-        coherent_store2(pml + 2 * h, __builtin_bit_cast(uint2, make_float2(any_bad ? nanv : big_m, any_bad ? nanv : l)));
+        coherent_store2_at(pml, h * 8, __builtin_bit_cast(uint2, make_float2(any_bad ? nanv : big_m, any_bad ? nanv : l)));
     }
   }
 
@@ -1729,10 +1731,15 @@ __global__ __launch_bounds__(kMergeGroups * 32) void merge_parts_kernel(
 
 // Most workgroups of the fixed-partition split per compute unit (one wave
 // each; the grid is also capped by the workspace's partitions per sequence).
-// Measured: 128 beats 32 and 64 (fewer items per workgroup, so the
-// dispatcher balances the tail) and 256 (a grid mostly past the batch's
-// items, whose workgroups only scan the lengths and leave).
+// Every workgroup finds its items by scanning the lengths from the batch's
+// start, 64 sequences per step, so the scan grows with the batch: up to 256
+// sequences 128 per compute unit beat 32 and 64 (fewer items per workgroup,
+// so the dispatcher balances the tail) and 256 (a grid mostly past the
+// batch's items); for larger batches 32 beat 128 (fewer workgroups
+// repeating long scans).
 constexpr int kSplitWgsPerCu = 128;
+constexpr int kSplitWgsPerCuLarge = 32;
+constexpr int kSplitLargeBatch = 256;      // sequences
 
 template <typename QS, typename KS, int GT, int BS, bool WIN>
 // The fields the launch's first loads depend on come as separate scalar
@@ -1799,7 +1806,8 @@ hipError_t launch_fast_bs(const DecodeArgs &a, hipStream_t s, const LaunchEvents
     const int64_t units = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * a.head_groups;
     const dim3 block(kSplitWaves * 64);
     const int64_t most = units * a.max_parts;
-    const dim3 sgrid(static_cast<unsigned>(min(most, static_cast<int64_t>(device_compute_units()) * kSplitWgsPerCu)));
+    const int per_cu = a.num_seqs <= kSplitLargeBatch ? kSplitWgsPerCu : kSplitWgsPerCuLarge;
+    const dim3 sgrid(static_cast<unsigned>(min(most, static_cast<int64_t>(device_compute_units()) * per_cu)));
     const dim3 mgrid(static_cast<unsigned>(units), static_cast<unsigned>(a.heads_per_wg));
     // lane groups per merge workgroup: enough for one round of loads (8
     // partitions a group) at the workspace's most partitions, at least 2

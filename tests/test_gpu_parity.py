@@ -371,7 +371,9 @@ def test_edge_lengths():
 def test_many_short_contexts(kv):
     """Over a thousand 1-2 tile contexts: in the balanced split a wave's tile
     range then spans about ten (sequence, head group) units, past the ones
-    whose q is staged ahead, with whole units and split ones mixed."""
+    whose q is staged ahead, with whole units and split ones mixed.  With
+    fixed partitions of one and two blocks, the split's workgroups find their
+    items across 19 chunks of 64 sequences (chunks passed four at a time)."""
     rng = np.random.default_rng(51)
     lens = rng.integers(1, 25, size=1200)
     need = sum(-(-int(n) // 16) for n in lens)
@@ -381,7 +383,7 @@ def test_many_short_contexts(kv):
         wl = W.build_decode(51, name="short", kv_dtype="bf16", **common)
     else:
         wl = W.build_write_filled(51, name="short-fp8", src_dtype="bf16", kv_dtype="fp8_e4m3", **common)
-    check_decode(wl, parts=(0, pa.PA_PARTITION_AUTO))
+    check_decode(wl, parts=(0, 16, 32, pa.PA_PARTITION_AUTO))
 
 
 def test_out_of_range_table_entry_and_length_give_nan_rows():

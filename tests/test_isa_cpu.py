@@ -104,3 +104,35 @@ def test_prefill_kernels_keep_three_waves_per_simd_without_scratch(prefill_resou
     for name, (vgpr, scratch) in pf.items():
         assert scratch == 0, (name, scratch)
         assert vgpr <= PREFILL_MAX_VGPRS, (name, vgpr)
+
+
+@pytest.fixture(scope="module", params=[0, 2], ids=["bf16-bf16", "bf16-fp8"])
+def decode_resources(request, tmp_path_factory):
+    out = tmp_path_factory.mktemp("isa") / "df.o"
+    cmd = [B.hipcc(), *B.FLAGS, f"-DPA_FAST_COMBO={request.param}", "--cuda-device-only", "-c",
+           os.path.join(B.PKG, "csrc", "pa_decode_fast.hip"), "-o", str(out),
+           "-Rpass-analysis=kernel-resource-usage"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        pytest.skip("hipcc unavailable: " + res.stderr[-300:])
+    kernels = {}
+    for block in res.stderr.split("Function Name: ")[1:]:
+        name = block.split()[0]
+        scratch = int(re.search(r"ScratchSize \[bytes/lane\]: (\d+)", block).group(1))
+        kernels[name] = scratch
+    return kernels
+
+
+def test_decode_kernels_use_no_scratch(decode_resources):
+    """Every head-dim-128 decode kernel (the balanced split, the single pass,
+    the fixed split at its three waves per SIMD, the merge) fits its
+    registers: a spill to scratch memory in the fixed split's item search
+    once made that kernel a quarter slower."""
+    kinds = ("decode_pair_kernel", "decode_fast_kernel", "decode_split_kernel", "merge_parts_kernel")
+    found = {k: 0 for k in kinds}
+    for name, scratch in decode_resources.items():
+        for k in kinds:
+            if k in name:
+                found[k] += 1
+                assert scratch == 0, (name, scratch)
+    assert all(found.values()), found
