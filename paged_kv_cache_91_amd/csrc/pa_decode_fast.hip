@@ -1805,7 +1805,12 @@ hipError_t launch_fast_bs(const DecodeArgs &a, hipStream_t s, const LaunchEvents
   if (a.partition_size > 0) {
     const int64_t units = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * a.head_groups;
     const dim3 block(kSplitWaves * 64);
-    const int64_t most = units * a.max_parts;
+    // a window of W positions spans at most (W - 1) / P + 2 partitions, far
+    // fewer than the table's width allows; workgroups past the batch's
+    // items only scan the lengths and leave
+    int64_t parts = a.max_parts;
+    if (a.window > 0) parts = min(parts, static_cast<int64_t>((a.window - 1) / a.partition_size + 2));
+    const int64_t most = units * parts;
     const int per_cu = a.num_seqs <= kSplitLargeBatch ? kSplitWgsPerCu : kSplitWgsPerCuLarge;
     const dim3 sgrid(static_cast<unsigned>(min(most, static_cast<int64_t>(device_compute_units()) * per_cu)));
     const dim3 mgrid(static_cast<unsigned>(units), static_cast<unsigned>(a.heads_per_wg));
