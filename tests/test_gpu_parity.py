@@ -611,3 +611,17 @@ def test_timed_decode_records_its_kernels(part):
     say(f"    partition {part}: kernels {kernel_ms * 1e3:.1f} us, bracket {bracket_ms * 1e3:.1f} us")
     assert 0 < kernel_ms <= bracket_ms
     assert max_err(out_f64(out), ref) <= 2e-2
+    # the same with the timing-only events bench.py hands to the hook
+    import bench
+    t0, t1 = bench.TimingEvent(), bench.TimingEvent()
+    out.fill_(float("nan"))
+    b0.record(st)
+    pa.pa_time_next_decode(t0, t1)
+    pa.pa_decode(dev.q, dev.pool, dev.tables, dev.ctx, wl.scale, out=out, partition_size=part,
+                 workspace=ws, q_dtype=wl.q_dtype, stream=st)
+    b1.record(st)
+    torch.cuda.synchronize()
+    timing_ms, bracket_ms = t0.elapsed_time(t1), b0.elapsed_time(b1)
+    say(f"    partition {part}: kernels (timing-only events) {timing_ms * 1e3:.1f} us")
+    assert 0 < timing_ms <= bracket_ms
+    assert max_err(out_f64(out), ref) <= 2e-2
