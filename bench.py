@@ -397,6 +397,53 @@ def cpu_baseline(wl, new_k, new_v, nseq, min_seconds=10.0, max_passes=50):
             "decode_tokens_per_s_per_layer": round(len(idx) / dt, 3)}
 
 
+def _oracle_threads(cores):
+    from threadpoolctl import threadpool_info
+    return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+
+
+def decode_cpu_baseline(wl, window, W, min_seconds=5.0, max_passes=200, pair_budget=2_000_000):
+    """The float64 oracle's decode on a bounded sample of the same batch: the
+    first sequences up to about ``pair_budget`` (position, query head) pairs,
+    on the pools as the GPU decode reads them (the workload's cache write for
+    those sequences, or its block copies, applied first and not timed, as
+    on the GPU line), repeated until about ``min_seconds`` have been timed."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    seen = [min(int(n), window) if window else int(n) for n in wl.context_lens]
+    k, pairs = 0, 0
+    while k < wl.num_seqs and (k == 0 or pairs + seen[k] * wl.num_q_heads <= pair_budget):
+        pairs += seen[k] * wl.num_q_heads
+        k += 1
+    idx = np.arange(k)
+    kp, vp = wl.k_pool, wl.v_pool
+    with threadpool_limits(limits=cores):
+        threads = _oracle_threads(cores)
+        if wl.write_k is not None:
+            bs = wl.block_size
+            mine = np.isin(wl.slot_mapping // bs, wl.block_tables[idx].ravel())
+            kp, vp = oracle.oracle_write(wl.write_k[mine], wl.write_v[mine], wl.write_src_dtype,
+                                         wl.slot_mapping[mine], kp, vp, wl.kv_dtype, wl.k_scale, wl.v_scale)
+        if wl.copy_pairs is not None:
+            kp, vp = oracle.oracle_copy(kp, vp, wl.copy_pairs)
+        passes, total = 0, 0.0
+        while total < min_seconds and passes < max_passes:
+            t0 = time.perf_counter()
+            oracle.oracle_decode(wl.q[idx], wl.q_dtype, kp, vp, wl.kv_dtype, wl.block_tables[idx],
+                                 wl.context_lens[idx], wl.scale, wl.k_scale, wl.v_scale, window=window)
+            total += time.perf_counter() - t0
+            passes += 1
+    dt = total / passes
+    kv = sum(seen[:k]) * 2 * wl.num_kv_heads * wl.head_dim * W.ELEMENT_SIZE[wl.kv_dtype]
+    return {"value": round(kv / dt / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{passes} passes of the decode of the first {k} of {wl.num_seqs} sequences "
+                      f"({sum(seen[:k])} positions, float64 numpy), {total:.1f}s in total"}
+
+
 def other_workload(args, pa, W, torch, dev):
     """pa_decode alone on one of the other batches, timed per call (after its
     cache write or block copies, which are not timed) by the event pair the
@@ -454,6 +501,7 @@ def other_workload(args, pa, W, torch, dev):
     parts = [-1, 0] + ([wl.partition_size] if wl.partition_size > 0 else [256])
     if args.partitions:
         parts = [int(x) for x in args.partitions.split(",")]
+    cpu = None if args.no_cpu_baseline else decode_cpu_baseline(wl, window, W)
     for part in parts:
         ws = pa.new_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                               wl.max_blocks_per_seq, wl.block_size, part, device=dev) if part else None
@@ -500,6 +548,7 @@ def other_workload(args, pa, W, torch, dev):
             "kv_gbs": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "decode_tokens_per_s_per_layer": round(wl.num_seqs / (med * 1e-6), 1),
             "cache": "warm (fits the last-level cache)" if kv_bytes < (256 << 20) else "pools exceed the last-level cache",
+            "cpu_baseline": cpu,
         }), flush=True)
 
 
@@ -568,6 +617,27 @@ def prefill_workload(args, pa, W, torch, dev):
     med = us[len(us) // 2]
     tflops = flops / (med * 1e-6) / 1e12
     assert bool(torch.isfinite(out.float()).all()), "non-finite output"
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the float64 oracle on the batch's first sequence, passes until ~5 s
+        import oracle
+        from threadpoolctl import threadpool_limits
+        cores = len(os.sched_getaffinity(0))
+        L0, n0 = int(qlens[0]), int(lens[0])
+        pairs0 = sum(range(n0 - L0 + 1, n0 + 1))
+        passes, total = 0, 0.0
+        with threadpool_limits(limits=cores):
+            threads = _oracle_threads(cores)
+            while total < 5.0 and passes < 20:
+                t0 = time.perf_counter()
+                oracle.oracle_prefill(q_host[:L0], "bf16", wl.k_pool, wl.v_pool, "bf16", wl.block_tables[:1],
+                                      lens[:1], np.array([0, L0]), wl.scale)
+                total += time.perf_counter() - t0
+                passes += 1
+        cpu = {"value": round(pairs0 * 32 * 4 * 128 / (total / passes) / 1e12, 6), "unit": "TFLOP/s",
+               "cores": threads, "kind": "oracle",
+               "sample": f"{passes} passes of the batch's first sequence ({L0} queries over {n0} positions, "
+                         f"float64 numpy), {total:.1f}s in total"}
     print(json.dumps({
         "workload": args.workload, "num_seqs": S, "query_rows": T, "context_tokens": int(lens.sum()),
         "attended_pairs": pairs, "flops": flops,
@@ -576,6 +646,7 @@ def prefill_workload(args, pa, W, torch, dev):
         "tflops": round(tflops, 1), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
         "frac_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "tokens_per_s_per_layer": round(T / (med * 1e-6), 1),
+        "cpu_baseline": cpu,
     }), flush=True)
 
 
