@@ -695,8 +695,26 @@ def swap_workload(args, pa, torch, dev):
         med = timed(fn, reps)
         res[name] = {"median_us": round(med, 1), "gbs": round(total / (med * 1e-6) / 1e9, 2)}
         log(f"[bench] swap {name}: {med:.1f} us")
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle's block copy between host arrays of the two pools' shapes
+        # (device pool to swap area), passes until about 5 s
+        import oracle
+        src_k = np.zeros((nb_dev, 8, 16, 128), dtype=np.uint16)
+        src_v = np.zeros_like(src_k)
+        dst_k = np.zeros((nb_host, 8, 16, 128), dtype=np.uint16)
+        dst_v = np.zeros_like(dst_k)
+        passes, spent = 0, 0.0
+        while spent < 5.0 and passes < 200:
+            t0 = time.perf_counter()
+            oracle.oracle_swap(src_k, src_v, dst_k, dst_v, out_pairs)
+            spent += time.perf_counter() - t0
+            passes += 1
+        cpu = {"value": round(total / (spent / passes) / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{passes} passes of the same {moved}-block copy between host arrays (numpy), "
+                         f"{spent:.1f}s in total"}
     print(json.dumps({"workload": "swap", "blocks_per_call": moved, "bytes_per_call": total,
-                      "block_bytes": block_bytes, "calls": reps, "results": res}), flush=True)
+                      "block_bytes": block_bytes, "calls": reps, "results": res, "cpu_baseline": cpu}), flush=True)
 
 
 def calibrate_copy(mib, pa, torch, dev):
