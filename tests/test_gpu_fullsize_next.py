@@ -5,14 +5,15 @@ launch configurations:
   positions, the Llama-3-8B layer shape, W = 4096), balanced split, single
   pass and fixed 512-position partitions, with every table entry of a block
   wholly before a sequence's window set to -1 and its contents NaN (released
-  blocks: never read); 8 sequences compared with the oracle (the shortest,
-  the longest, random others), every output checked finite;
+  blocks: never read); every sequence compared with the oracle, every output
+  checked finite;
 * prefill on 16 whole prompts of 2048 positions and on 16 chunks of 512
   queries after cached prefixes of 0 .. 3584 positions (the same shape):
-  96 query rows sampled across every sequence (its first and last query,
-  block edges, random others), each compared with the oracle on its own
-  (a query at position p is a one-query prefill over positions 0 .. p
-  through the same table), every output checked finite.
+  every query row of the first sequence (the oracle's prefill of that whole
+  sequence) and 90 more sampled across the others (first and last query,
+  block edges, random others), each compared with the oracle on its own (a
+  query at position p is a one-query prefill over positions 0 .. p through
+  the same table), every output checked finite.
 
 The inputs follow bench.py's recipe for those workloads (same seeds, same
 generators).  Each ``MARGIN`` line records the measured error against its
@@ -59,9 +60,7 @@ def test_window_decode_full():
             kp[dead] = NAN_BF16
             vp[dead] = NAN_BF16
             tables[s, :lo // bs] = -1
-    order = np.argsort(wl.context_lens, kind="stable")
-    rng = np.random.default_rng(91)
-    seqs = sorted({int(order[0]), int(order[-1])} | set(int(x) for x in rng.choice(len(order), 6, replace=False)))
+    seqs = list(range(wl.num_seqs))
     ref = np.stack([oracle.oracle_decode(sub.q, sub.q_dtype, sub.k_pool, sub.v_pool, sub.kv_dtype, sub.block_tables,
                                          sub.context_lens, sub.scale, window=window)[0]
                     for sub in (subset(wl, [s]) for s in seqs)])
@@ -105,16 +104,19 @@ def test_prefill_full(kind):
     got = out_f64(pa.pa_prefill(qd, dev.pool, dev.tables, dev.ctx, torch.from_numpy(qs).to(DEV), wl.scale,
                                 out=out, q_dtype="bf16"))
     assert np.isfinite(got).all()
-    # sampled rows: per sequence its first and last query, queries at block
-    # edges, and random others (96 in all)
+    # the first sequence whole
+    a0, b0 = int(qs[0]), int(qs[1])
+    whole = oracle.oracle_prefill(q[a0:b0], "bf16", wl.k_pool, wl.v_pool, "bf16", wl.block_tables[:1],
+                                  wl.context_lens[:1], np.array([0, b0 - a0]), wl.scale)
+    errs = [max_err(got[a0:b0], whole)]
+    # sampled rows of the others: per sequence its first and last query,
+    # queries at block edges, and random others (90 in all)
     rng = np.random.default_rng(131)
     rows = []
-    for s in range(len(wl.context_lens)):
+    for s in range(1, len(wl.context_lens)):
         a, b = int(qs[s]), int(qs[s + 1])
         picks = {a, b - 1, min(b - 1, a + 15), min(b - 1, a + 16)} | set(int(x) for x in rng.integers(a, b, 2))
         rows += sorted(picks)[:6]
-    rows = rows[:96]
-    errs = []
     for row in rows:
         s = int(np.searchsorted(qs, row, side="right") - 1)
         n, L = int(wl.context_lens[s]), int(qs[s + 1] - qs[s])
@@ -123,5 +125,5 @@ def test_prefill_full(kind):
                                     np.array([p + 1]), np.array([0, 1]), wl.scale)
         errs.append(max_err(got[row:row + 1], ref))
     err = max(errs)
-    margin(kind, "-", len(rows), err, tol_for(wl))
+    margin(kind, "-", (b0 - a0) + len(rows), err, tol_for(wl))
     assert err <= tol_for(wl), err
